@@ -1,0 +1,86 @@
+"""Seeded synthetic inputs for exact attention forward.
+
+This module only draws random numbers and names workloads; it holds none of
+the attention arithmetic. Both the GPU path's tests/bench and the CPU oracle
+are fed from here, so they see identical bits.
+
+Recipe: Q, K, V drawn i.i.d. N(0,1) in float32 from ``torch.Generator('cpu')``
+seeded with ``seed``, in the order Q, K, V, each ``[B, H, N, d]`` contiguous;
+optionally multiplied by ``value_scale`` in float32; then rounded to the
+target dtype with round-to-nearest-even (``Tensor.to``). The unit-variance
+inputs are the setting in which the cishoon.github.io "flashattention" post,
+section 1.1.2 item 2, derives that q.k/sqrt(d) has variance 1.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: torch.dtype
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    value_scale: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        """Default softmax scale 1/sqrt(d), as the fp32 value both sides use."""
+        return float(torch.tensor(1.0 / (self.d ** 0.5), dtype=torch.float32).item())
+
+    def describe(self) -> str:
+        dt = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}[self.dtype]
+        c = "causal" if self.causal else "non-causal"
+        return f"{dt} {c} attention fwd B={self.B} H={self.H} N={self.N} d={self.d}"
+
+
+def _wl(cfg: int, variant: int, **kw) -> Workload:
+    return Workload(seed=1000 * cfg + variant, **kw)
+
+
+# The five workloads: a small fp32 case, an fp32 causal case, the bf16 causal
+# headline case, a long-context d=128 case (causal and not), and an fp16 case
+# with a ragged-tail variant.
+WORKLOADS = {
+    "c1_f32_small": _wl(1, 0, name="c1_f32_small", dtype=torch.float32,
+                        B=1, H=1, N=128, d=64, causal=False),
+    "c2_f32_causal": _wl(2, 0, name="c2_f32_causal", dtype=torch.float32,
+                         B=1, H=32, N=1024, d=64, causal=True),
+    "c3_bf16_causal": _wl(3, 0, name="c3_bf16_causal", dtype=torch.bfloat16,
+                          B=4, H=16, N=4096, d=64, causal=True),
+    "c4_bf16_d128_causal": _wl(4, 0, name="c4_bf16_d128_causal", dtype=torch.bfloat16,
+                               B=1, H=32, N=8192, d=128, causal=True),
+    "c4_bf16_d128": _wl(4, 1, name="c4_bf16_d128", dtype=torch.bfloat16,
+                        B=1, H=32, N=8192, d=128, causal=False),
+    "c5_f16": _wl(5, 0, name="c5_f16", dtype=torch.float16,
+                  B=1, H=8, N=16384, d=64, causal=False, value_scale=0.5),
+    "c5_f16_ragged": _wl(5, 1, name="c5_f16_ragged", dtype=torch.float16,
+                         B=1, H=8, N=16383, d=64, causal=False, value_scale=0.5),
+}
+
+HEADLINE = "c3_bf16_causal"
+
+
+def make_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
+             value_scale: float = 1.0):
+    """Draw Q, K, V (in that order) on the CPU; return dtype tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    out = []
+    for _ in range(3):
+        x = torch.randn((B, H, N, d), dtype=torch.float32, generator=g)
+        if value_scale != 1.0:
+            x = x * torch.tensor(value_scale, dtype=torch.float32)
+        out.append(x.to(dtype).contiguous())
+    return tuple(out)
+
+
+def workload_inputs(w: Workload):
+    return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.value_scale)

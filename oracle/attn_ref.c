@@ -1,0 +1,275 @@
+/*
+ * attn_ref.c — CPU fp64 oracle for exact attention forward.
+ *
+ * TEST INFRASTRUCTURE: a plain, slow, obviously correct implementation of
+ * the attention definition. Only the test suite, the smoke check and the
+ * bench's CPU-baseline leg load it. It shares no code with the GPU library.
+ *
+ * What it computes is the plain definition, written out step by step:
+ *   [naive-attn] cishoon.github.io "flashattention" post, section 1.1.2:
+ *     Attention(Q,K,V) = softmax(Q K^T / sqrt(d)) V, the softmax taken per
+ *     row over the key axis, made safe by subtracting the row maximum
+ *     (item 3), and o_i = sum_j alpha_ij v_j (item 4). Section 2 spells out
+ *     the same three steps as separate materialised passes (scores, softmax,
+ *     P.V); this file keeps that order for one query row at a time.
+ *   [v2-naive] "Flash Attention（二）v2版本朴素实现 cuda core", section 3.3:
+ *     the scale is multiplied into the score; section 3.4: query row i sees
+ *     key j only when j <= i under the causal mask (diagonal included).
+ *   [FA2-principles] "Flash Attention v2 的核心优化原理与工程实现", section 4:
+ *     the row statistics (max and sum) are written next to O; they are
+ *     returned here folded into one log-sum-exp, lse_i = m_i + ln(l_i).
+ *
+ * The scale is the caller's fp32 value widened to double, so that the oracle
+ * and any other implementation use the identical number.
+ *
+ * Pinned by tests/test_oracle_pins.py against closed forms, invariants the
+ * pages state (rows of P sum to 1, constant V, Q = 0 mean, unit-basis probe,
+ * causal row 0, N = 1 and N = 2 closed forms), brute force on tiny inputs
+ * against a library softmax, and the pages' printed worked values.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#include "../include/attn_ref.h"
+
+/* ---- exact decoding of the input formats ------------------------------ */
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 mantissa bits. */
+static double decode_f16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* zero / subnormal */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);     /* (1.m) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+static double decode_bf16(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static double decode_one(const void* base, int64_t idx, int dtype)
+{
+    if (dtype == ATTN_REF_F32) {
+        float f;
+        memcpy(&f, (const char*)base + idx * 4, 4);
+        return (double)f;
+    }
+    uint16_t h;
+    memcpy(&h, (const char*)base + idx * 2, 2);
+    return dtype == ATTN_REF_F16 ? decode_f16(h) : decode_bf16(h);
+}
+
+int attn_ref_decode(const void* src, double* dst, int64_t n, int dtype)
+{
+    if (!src || !dst || n < 0)
+        return ATTN_REF_EINVAL;
+    if (dtype != ATTN_REF_F32 && dtype != ATTN_REF_F16 && dtype != ATTN_REF_BF16)
+        return ATTN_REF_EINVAL;
+    for (int64_t i = 0; i < n; i++)
+        dst[i] = decode_one(src, i, dtype);
+    return ATTN_REF_OK;
+}
+
+/* ---- one query row, straight from the definition ----------------------- */
+
+typedef struct {
+    const void *q, *k, *v;
+    int64_t B, H, N, d;
+    int causal;
+    double scale;
+    int dtype;
+    const int64_t* rows;   /* flat row ids */
+    int64_t n_rows;
+    double* o;             /* [n_rows, d] */
+    double* lse;           /* [n_rows] or NULL */
+    int64_t next;          /* shared work counter */
+    int failed;
+} job_t;
+
+/* Computes output row `t` of the job: query row r = rows[t].
+ * s_row has room for N doubles, qrow for d doubles. */
+static void one_row(job_t* jb, int64_t t, double* s_row, double* qrow)
+{
+    const int64_t N = jb->N, d = jb->d;
+    const int64_t r = jb->rows[t];
+    const int64_t bh = r / N;          /* (b*H + h) */
+    const int64_t i = r % N;           /* query position */
+    const int64_t slice = bh * N * d;  /* element offset of the (b,h) slice */
+
+    /* visible keys: j in [0, n_vis) */
+    const int64_t n_vis = jb->causal ? i + 1 : N;
+
+    for (int64_t c = 0; c < d; c++)
+        qrow[c] = decode_one(jb->q, slice + i * d + c, jb->dtype);
+
+    /* step 1: scores s_ij = scale * (q_i . k_j), one materialised row of S */
+    for (int64_t j = 0; j < n_vis; j++) {
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; c++)
+            dot += qrow[c] * decode_one(jb->k, slice + j * d + c, jb->dtype);
+        s_row[j] = jb->scale * dot;
+    }
+
+    /* step 2: safe softmax over the row */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n_vis; j++)
+        if (s_row[j] > m)
+            m = s_row[j];
+    double l = 0.0;
+    for (int64_t j = 0; j < n_vis; j++) {
+        s_row[j] = exp(s_row[j] - m);   /* e_ij, overwrites s_ij */
+        l += s_row[j];
+    }
+    for (int64_t j = 0; j < n_vis; j++)
+        s_row[j] = s_row[j] / l;        /* p_ij */
+
+    /* step 3: o_i = sum_j p_ij v_j */
+    double* o = jb->o + t * d;
+    for (int64_t c = 0; c < d; c++)
+        o[c] = 0.0;
+    for (int64_t j = 0; j < n_vis; j++) {
+        const double p = s_row[j];
+        for (int64_t c = 0; c < d; c++)
+            o[c] += p * decode_one(jb->v, slice + j * d + c, jb->dtype);
+    }
+
+    if (jb->lse)
+        jb->lse[t] = m + log(l);
+}
+
+static void* worker(void* arg)
+{
+    job_t* jb = (job_t*)arg;
+    double* s_row = (double*)malloc((size_t)jb->N * sizeof(double));
+    double* qrow = (double*)malloc((size_t)jb->d * sizeof(double));
+    if (!s_row || !qrow) {
+        __atomic_store_n(&jb->failed, 1, __ATOMIC_SEQ_CST);
+        free(s_row);
+        free(qrow);
+        return NULL;
+    }
+    for (;;) {
+        int64_t t = __atomic_fetch_add(&jb->next, 1, __ATOMIC_RELAXED);
+        if (t >= jb->n_rows)
+            break;
+        one_row(jb, t, s_row, qrow);
+    }
+    free(s_row);
+    free(qrow);
+    return NULL;
+}
+
+static int check_args(const void* q, const void* k, const void* v,
+                      int64_t B, int64_t H, int64_t N, int64_t d,
+                      int causal, float scale, int dtype)
+{
+    if (!q || !k || !v)
+        return ATTN_REF_EINVAL;
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0)
+        return ATTN_REF_EINVAL;
+    if (causal != 0 && causal != 1)
+        return ATTN_REF_EINVAL;
+    if (!isfinite(scale))
+        return ATTN_REF_EINVAL;
+    if (dtype != ATTN_REF_F32 && dtype != ATTN_REF_F16 && dtype != ATTN_REF_BF16)
+        return ATTN_REF_EINVAL;
+    /* B*H*N*d must be addressable */
+    if (B > INT64_MAX / H || B * H > INT64_MAX / N || B * H * N > INT64_MAX / d / 4)
+        return ATTN_REF_EINVAL;
+    return ATTN_REF_OK;
+}
+
+static int run_job(job_t* jb, int num_threads)
+{
+    if (num_threads <= 0) {
+        long n = sysconf(_SC_NPROCESSORS_ONLN);
+        num_threads = n > 0 ? (int)n : 1;
+    }
+    if (num_threads > jb->n_rows)
+        num_threads = (int)(jb->n_rows > 0 ? jb->n_rows : 1);
+
+    pthread_t* th = (pthread_t*)malloc((size_t)num_threads * sizeof(pthread_t));
+    if (!th)
+        return ATTN_REF_ENOMEM;
+    int started = 0;
+    for (int t = 0; t < num_threads; t++) {
+        if (pthread_create(&th[t], NULL, worker, jb) != 0)
+            break;
+        started++;
+    }
+    if (started == 0)
+        worker(jb);   /* no thread could start: do the work here */
+    for (int t = 0; t < started; t++)
+        pthread_join(th[t], NULL);
+    free(th);
+    return jb->failed ? ATTN_REF_ENOMEM : ATTN_REF_OK;
+}
+
+int attn_fwd_ref_rows(const void* q, const void* k, const void* v,
+                      int64_t B, int64_t H, int64_t N, int64_t d,
+                      int causal, float scale, int dtype,
+                      const int64_t* rows, int64_t n_rows,
+                      double* o_rows, double* lse_rows, int num_threads)
+{
+    int rc = check_args(q, k, v, B, H, N, d, causal, scale, dtype);
+    if (rc != ATTN_REF_OK)
+        return rc;
+    if (n_rows < 0 || (n_rows > 0 && (!rows || !o_rows)))
+        return ATTN_REF_EINVAL;
+    for (int64_t t = 0; t < n_rows; t++)
+        if (rows[t] < 0 || rows[t] >= B * H * N)
+            return ATTN_REF_EINVAL;
+    if (n_rows == 0)
+        return ATTN_REF_OK;
+
+    job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.q = q; jb.k = k; jb.v = v;
+    jb.B = B; jb.H = H; jb.N = N; jb.d = d;
+    jb.causal = causal;
+    jb.scale = (double)scale;
+    jb.dtype = dtype;
+    jb.rows = rows;
+    jb.n_rows = n_rows;
+    jb.o = o_rows;
+    jb.lse = lse_rows;
+    return run_job(&jb, num_threads);
+}
+
+int attn_fwd_ref(const void* q, const void* k, const void* v,
+                 double* o_ref, double* lse_ref,
+                 int64_t B, int64_t H, int64_t N, int64_t d,
+                 int causal, float scale, int dtype, int num_threads)
+{
+    int rc = check_args(q, k, v, B, H, N, d, causal, scale, dtype);
+    if (rc != ATTN_REF_OK)
+        return rc;
+    if (!o_ref)
+        return ATTN_REF_EINVAL;
+    const int64_t n = B * H * N;
+    int64_t* rows = (int64_t*)malloc((size_t)n * sizeof(int64_t));
+    if (!rows)
+        return ATTN_REF_ENOMEM;
+    for (int64_t r = 0; r < n; r++)
+        rows[r] = r;   /* every row, in storage order: o_rows == o_ref */
+    rc = attn_fwd_ref_rows(q, k, v, B, H, N, d, causal, scale, dtype,
+                           rows, n, o_ref, lse_ref, num_threads);
+    free(rows);
+    return rc;
+}
