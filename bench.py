@@ -1,0 +1,195 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+A step is one attention forward (one launch of the fused kernel) over the
+workload's synthetic inputs, which are resident in HBM before timing starts.
+Default workload: bf16, causal, B=4, H=16, N=4096, d=64.
+
+Prints ONE JSON line with the attention TFLOPS, its roofline fraction and
+the CPU fp64 oracle timed on a bounded sample of the same workload.
+
+FLOP convention (every page's): 4*B*H*N^2*d per forward, halved for causal —
+checked against the figures printed in "Flash Attention（二）v2版本朴素实现
+cuda core", section 4.1, and in the final table of "Flash Attention CUDA
+Kernel 优化: 从 56 到 986 TFLOPS on B300 — G7: 回归 1CTA".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth.
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+DTYPE_NAME = {"torch.bfloat16": "bf16", "torch.float16": "fp16", "torch.float32": "fp32"}
+
+COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_counters.json")
+KERNEL_SOURCES = ["exact_attention_15_amd/csrc/fwd_mfma16.hip",
+                  "exact_attention_15_amd/csrc/fwd_f32.hip",
+                  "exact_attention_15_amd/csrc/attn_api.hip",
+                  "exact_attention_15_amd/csrc/attn_internal.h"]
+
+
+def attention_flops(B, H, N, d, causal) -> float:
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def algorithmic_bytes(B, H, N, d, elem_bytes) -> int:
+    """Q, K, V read once, O written once, plus the fp32 lse row statistic."""
+    return 4 * B * H * N * d * elem_bytes + 4 * B * H * N
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counters, or None when absent or taken on other kernel sources."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    with open(COUNTER_FILE) as f:
+        data = json.load(f)
+    entry = data.get(workload)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return entry["hbm_bytes_per_launch"]
+
+
+def cpu_baseline(w, q, k, v, n_slices: int):
+    import numpy as np
+    import oracle
+
+    oracle.build() if not os.path.exists(oracle.LIB_PATH) else None
+    threads = len(os.sched_getaffinity(0))
+    rows = np.arange(n_slices * w.N, dtype=np.int64)   # every row of the first slices
+    t0 = time.perf_counter()
+    oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows, num_threads=threads)
+    dt = time.perf_counter() - t0
+    flops = attention_flops(1, n_slices, w.N, w.d, w.causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{n_slices} of {w.B * w.H} (b,h) slices, all {w.N} rows each "
+                      f"({flops / 1e9:.1f} GFLOP by the same convention), {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-slices", type=int, default=16,
+                    help="(b,h) slices the CPU oracle baseline runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true", help="skip the sampled parity gate")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by (b,h) slices with no exchange, but no multi-GPU run exists)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_15_amd as ea
+    from exact_attention_15_amd.inputs import HEADLINE, WORKLOADS, workload_inputs
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    dt_name = DTYPE_NAME[str(w.dtype)]
+    ea.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    q, k, v = workload_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    out = (o, lse)
+
+    for _ in range(args.warmup):
+        ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+
+    parity = None
+    if not args.no_check:
+        import oracle
+        rng = np.random.default_rng(1)
+        rows = np.unique(np.concatenate([np.arange(8), rng.integers(0, w.B * w.H * w.N, 56)]))
+        o_ref, l_ref = oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows)
+        o_got = o.cpu().double().numpy().reshape(-1, w.d)[rows]
+        parity = float(np.abs(o_got - o_ref).max())
+        tol = 1e-4 if dt_name == "fp32" else 2e-2
+        if not parity <= tol:
+            print(f"bench.py: parity gate failed: O max-abs {parity:.3e} > {tol}", file=sys.stderr)
+            sys.exit(1)
+
+    # Timed region: barrier-equivalent sync, K launches bracketed by HIP events
+    # recorded on the stream the kernels run on, sync.
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+
+    flops = attention_flops(w.B, w.H, w.N, w.d, w.causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    elem = 4 if dt_name == "fp32" else 2
+    abytes = algorithmic_bytes(w.B, w.H, w.N, w.d, elem)
+    peak = PEAK_TFLOPS[dt_name]
+    traffic = measured_traffic(name)
+
+    line = {
+        "metric": "attention fwd TFLOPS (bf16, causal, N=4096 d=64); % of MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name,
+        "data": "synthetic (seeded i.i.d. N(0,1) inputs rounded to the dtype)",
+        "config": {"workload": w.describe(), "name": name, "B": w.B, "H": w.H, "N": w.N,
+                   "d": w.d, "causal": w.causal, "scale": w.scale},
+        "pct_of_peak": round(100 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": traffic},
+        "algorithmic_gb_s": round(abytes / (ms * 1e-3) / 1e9, 1),
+        "exp_per_s": (w.B * w.H * w.N * w.N / (2 if w.causal else 1)) / (ms * 1e-3),
+        "parity_o_max_abs_sampled": parity,
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        n_sl = max(1, min(args.cpu_slices, w.B * w.H))
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, n_sl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

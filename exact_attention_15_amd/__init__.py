@@ -1,0 +1,114 @@
+"""Exact attention forward for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libattn.so`` (``include/attn.h``):
+it checks tensors, allocates the outputs with torch on the inputs' device
+and passes raw pointers plus torch's current HIP stream. Every step of the
+computation runs in the library's HIP kernels; there is no fallback path,
+and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EALIGN, ATTN_EHIP = 0, -1, -2, -3, -4
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"attn_fwd failed ({code}): {msg}")
+        self.code = code
+
+
+def load_library():
+    """Load libattn.so (built by ``exact_attention_15_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m exact_attention_15_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                             ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_strerror.argtypes = [ctypes.c_int]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().attn_strerror(int(code)).decode()
+
+
+def dtype_code(dtype) -> int:
+    import torch
+    m = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+    if dtype not in m:
+        raise TypeError(f"unsupported dtype {dtype}; need float32, float16 or bfloat16")
+    return m[dtype]
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded to fp32 (the value the library multiplies in)."""
+    import struct
+    return struct.unpack("f", struct.pack("f", 1.0 / math.sqrt(d)))[0]
+
+
+def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> int:
+    """Raw C-ABI call with integer pointers; returns the library's code."""
+    return load_library().attn_fwd(q, k, v, o, lse, B, H, N, d, int(causal),
+                                   float(scale), int(dtype), stream)
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None):
+    """O, lse = attention forward of q, k, v ([B,H,N,d] device tensors).
+
+    Returns ``o`` (same dtype/shape as q) and ``lse`` (float32 [B,H,N],
+    natural-log log-sum-exp of the scaled scores). ``out`` may pass
+    preallocated ``(o, lse)`` tensors.
+    """
+    import torch
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if q.device.type != "cuda" or k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one GPU device")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+            raise ValueError("out[0] must match q")
+        if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+                or lse.device != q.device:
+            raise ValueError("out[1] must be float32 [B, H, N] on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      B, H, N, d, causal, scale, dtype_code(q.dtype), stream)
+    if rc != ATTN_OK:
+        raise AttnError(rc, strerror(rc))
+    return o, lse
+
+
+__all__ = ["fwd", "attn_fwd", "load_library", "strerror", "AttnError", "default_scale",
+           "dtype_code", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

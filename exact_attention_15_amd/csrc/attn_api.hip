@@ -1,0 +1,72 @@
+// attn_api.hip — the C ABI of libattn.so: argument validation, dispatch on
+// (dtype, head dim, causal) and launch on the caller's stream.
+//
+// Validation happens before any HIP call, so an error code means nothing was
+// enqueued. The library keeps no state and allocates nothing.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale, int dtype) {
+    if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
+    if (B < 1 || H < 1 || N < 1) return ATTN_EINVAL;
+    if (causal != 0 && causal != 1) return ATTN_EINVAL;
+    if (!isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
+    // Positions are 32-bit inside the kernels; the grid is one-dimensional.
+    if (N > (int64_t)INT32_MAX - attn::kBlockM) return ATTN_EINVAL;
+    if (B > INT32_MAX / H) return ATTN_EINVAL;
+    const int64_t n_qtiles = (N + attn::kBlockM - 1) / attn::kBlockM;
+    if (n_qtiles * B * H > (int64_t)INT32_MAX) return ATTN_EINVAL;
+    if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+    const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
+    if (mis != 0 || ((uintptr_t)lse & 3u) != 0) return ATTN_EALIGN;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                        int dtype, void* stream) {
+    const int rc = validate(q, k, v, o, lse, B, H, N, d, causal, scale, dtype);
+    if (rc != ATTN_OK) return rc;
+
+    attn::FwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.N = N;
+    p.BH = (int)(B * H);
+    p.n_qtiles = (int)((N + attn::kBlockM - 1) / attn::kBlockM);
+    // scale * log2(e), rounded once to fp32: scores go straight into exp2.
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();   // clear a stale error so the launch is judged alone
+    hipError_t e;
+    if (dtype == ATTN_F32)
+        e = attn::launch_fwd32(p, (int)d, causal != 0, s);
+    else
+        e = attn::launch_fwd16(p, dtype == ATTN_BF16, (int)d, causal != 0, s);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+extern "C" const char* attn_strerror(int code) {
+    switch (code) {
+        case ATTN_OK: return "ok";
+        case ATTN_EINVAL: return "invalid argument";
+        case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128)";
+        case ATTN_EALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+        case ATTN_EHIP: return "HIP kernel launch failed";
+        default: return "unknown error code";
+    }
+}

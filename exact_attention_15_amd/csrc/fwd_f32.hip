@@ -1,0 +1,229 @@
+// fwd_f32.hip — fused attention forward for fp32 inputs on gfx950.
+//
+// Same method as the bf16/fp16 kernel (Q-tile outer loop, K/V-tile inner
+// loop, online softmax with deferred 1/l, causal tile skipping and diagonal
+// masking — "Flash Attention（二）v2版本朴素实现 cuda core", sections 1.1-1.4
+// and 3.2-3.5, whose kernel is itself fp32), with every product on the fp32
+// matrix cores (v_mfma_f32_32x32x2_f32): gfx950 has no reduced-precision
+// (xf32) fp32 MFMA, so scores and P.V are exact fp32 products accumulated in
+// fp32 and P is never rounded below fp32.
+//
+// Layout: 4 wave64s x 32 query rows; K/V tiles of 32 keys. One lane owns
+// one query, as in the 16-bit kernel:
+//   S^T[key][query] = K . Q^T : the contraction over d is split so that lane
+//       half g takes d in [g*D/2, (g+1)*D/2): each lane reads D/2 contiguous
+//       floats of a K row (16-byte LDS reads) and keeps D/2 floats of Q.
+//   O^T[d][query] += V^T . P^T : contraction step kk uses accumulator row kk
+//       of S^T as the B operand as is; the A operand is the matching key's V
+//       row, read straight from row-major LDS (lanes 0-31 read 32 consecutive
+//       floats of one key row).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr int kBlockN = 32;
+constexpr int kThreads = 256;
+
+template <int D>
+struct Smem32 {
+    static constexpr int kRowBytes = D * 4;
+    static constexpr int kTileBytes = kBlockN * D * 4;
+    static constexpr int kBytes = 4 * kTileBytes;   // K[2] + V[2]
+};
+
+// K rows: 16-byte chunk c of row r stored at chunk c ^ (r mod 8).
+template <int D>
+__device__ __forceinline__ int k_off32(int r, int c) {
+    return r * Smem32<D>::kRowBytes + ((c ^ (r & 7)) << 4);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdParams p) {
+    using S = Smem32<D>;
+    constexpr int CH = D / 4;                          // 16-byte chunks per row
+    constexpr int ITEMS = kBlockN * CH / kThreads;     // chunks per thread per tensor
+    constexpr int HALF = D / 2;
+    static_assert(ITEMS >= 1, "tile / thread mismatch");
+
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+
+    const int w = blockIdx.x;
+    const int tile = p.n_qtiles - 1 - w / p.BH;
+    const int bh = w - (w / p.BH) * p.BH;
+    const int N = (int)p.N;
+    const int q0 = tile * kBlockM;
+    const int qi = q0 + wave * 32 + l32;
+    const size_t base = (size_t)bh * (size_t)N * D;
+
+    const float* __restrict__ Qg = (const float*)p.q + base;
+    const float* __restrict__ Kg = (const float*)p.k + base;
+    const float* __restrict__ Vg = (const float*)p.v + base;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    // Q half-row of this lane: q[qi][g*D/2 .. g*D/2 + D/2 - 1].
+    float qf[HALF];
+#pragma unroll
+    for (int c = 0; c < HALF / 4; ++c) {
+        const f32x4 t = qi < N ? *(const f32x4*)(Qg + (size_t)qi * D + g * HALF + 4 * c) : zero4;
+        qf[4 * c + 0] = t[0];
+        qf[4 * c + 1] = t[1];
+        qf[4 * c + 2] = t[2];
+        qf[4 * c + 3] = t[3];
+    }
+
+    const int kv_end = CAUSAL ? min(q0 + kBlockM, N) : N;
+    const int n_tiles = (kv_end + kBlockN - 1) / kBlockN;
+
+    f32x4 kreg[ITEMS], vreg[ITEMS];
+    auto load_tile = [&](int kv0) {
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int item = tid + kThreads * it;
+            const int r = item / CH, c = item % CH;
+            const int key = kv0 + r;
+            kreg[it] = key < N ? *(const f32x4*)(Kg + (size_t)key * D + 4 * c) : zero4;
+            vreg[it] = key < N ? *(const f32x4*)(Vg + (size_t)key * D + 4 * c) : zero4;
+        }
+    };
+    auto store_tile = [&](int buf) {
+        char* ks = smem + buf * S::kTileBytes;
+        char* vs = smem + (2 + buf) * S::kTileBytes;
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int item = tid + kThreads * it;
+            const int r = item / CH, c = item % CH;
+            *(f32x4*)(ks + k_off32<D>(r, c)) = kreg[it];
+            *(f32x4*)(vs + r * S::kRowBytes + 16 * c) = vreg[it];
+        }
+    };
+
+    const float c2 = p.scale_log2;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int j = 0; j < n_tiles; ++j) {
+        const int cur = j & 1;
+        const int kv0 = j * kBlockN;
+        if (j + 1 < n_tiles) load_tile(kv0 + kBlockN);
+
+        const bool wave_live = !CAUSAL || kv0 <= q0 + wave * 32 + 31;
+        if (wave_live) {
+            const char* ks = smem + cur * S::kTileBytes;
+            const float* vs = (const float*)(smem + (2 + cur) * S::kTileBytes);
+
+            f32x16 s;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+            for (int c = 0; c < HALF / 4; ++c) {
+                const f32x4 a = *(const f32x4*)(ks + k_off32<D>(l32, g * (HALF / 4) + c));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf[4 * c + e], s, 0, 0, 0);
+            }
+
+            const bool diag = CAUSAL && (kv0 + kBlockN - 1 > q0);
+            const bool tail = kv0 + kBlockN > N;
+            if (diag || tail) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kv0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                    const bool dead = key >= N || (CAUSAL && key > qi);
+                    if (dead) s[i] = -INFINITY;
+                }
+            }
+
+            float mx = s[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx * c2);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+
+            float lsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_use));
+                lsum += s[i];
+            }
+            l_run = alpha * l_run + lsum;
+            m_run = m_new;
+
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+
+            // Step kk: lane half g contributes key 8(kk/4) + 4g + kk%4, whose
+            // probability is accumulator entry kk of this lane.
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                const int key = 8 * (kk >> 2) + 4 * g + (kk & 3);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const float a = vs[key * D + 32 * db + l32];
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kk], o[db], 0, 0, 0);
+                }
+            }
+        }
+
+        if (j + 1 < n_tiles) store_tile(cur ^ 1);
+        __syncthreads();
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.f / l_tot;
+    if (qi < N) {
+        float* Og = (float*)p.o + base + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int dd = 32 * db + 8 * i4 + 4 * g;
+                const f32x4 wv = {o[db][4 * i4] * inv, o[db][4 * i4 + 1] * inv,
+                                  o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv};
+                *(f32x4*)(Og + dd) = wv;
+            }
+        if (g == 0) p.lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const FwdParams& p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.n_qtiles * p.BH));
+    hipLaunchKernelGGL((fwd32_kernel<D, CAUSAL>), grid, dim3(kThreads), Smem32<D>::kBytes, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd32(const FwdParams& p, int d, bool causal, hipStream_t s) {
+    if (d == 64) return causal ? launch<64, true>(p, s) : launch<64, false>(p, s);
+    return causal ? launch<128, true>(p, s) : launch<128, false>(p, s);
+}
+
+}  // namespace attn

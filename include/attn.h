@@ -1,0 +1,86 @@
+/*
+ * attn.h — C ABI of the gfx950 (MI355X) exact attention forward library,
+ * libattn.so.
+ *
+ * The operation is the fused, tiled attention forward pass
+ *     O = softmax(scale * Q K^T [+ causal mask]) V
+ * together with the per-row log-sum-exp of the scaled scores.
+ *
+ * Sources (cited by page title and section):
+ *   [naive-attn]  cishoon.github.io, "flashattention" post, section 1.1.2:
+ *                 the attention formula, the 1/sqrt(d) scaling (item 2) and
+ *                 the row-wise safe softmax (item 3).
+ *   [v2-naive]    "Flash Attention（二）v2版本朴素实现 cuda core":
+ *                 section 1.1 (Q-tile outer loop, K/V-tile inner loop),
+ *                 1.2 (row max m and row sum l kept on chip), 1.3 (deferred
+ *                 1/l normalisation), 1.4 and 3.4 (causal: tiles above the
+ *                 diagonal skipped, the diagonal tile masked element-wise,
+ *                 row i sees keys j <= i), 3.2 (out-of-range keys zero-filled
+ *                 and masked), 3.5 (rows past N are not written).
+ *   [FA2-principles] "Flash Attention v2 的核心优化原理与工程实现", section 4:
+ *                 per-row statistics are written next to O (here folded into
+ *                 one log-sum-exp per row).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. lse is always fp32. */
+typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
+
+/* Return codes. */
+enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = -1,       /* bad argument (null pointer, size, dtype, scale, causal) */
+    ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128 */
+    ATTN_EALIGN = -3,       /* a base pointer not 16-byte aligned */
+    ATTN_EHIP = -4          /* the HIP launch failed */
+};
+
+/*
+ * attn_fwd — exact attention forward on the GPU.
+ *
+ * For every (b, h) slice and query row i < N:
+ *   o[b,h,i,:] = sum_j p_ij v[b,h,j,:],  p_ij = exp(s_ij - lse_i),
+ *   s_ij = scale * q[b,h,i,:] . k[b,h,j,:],
+ *   lse[b,h,i] = ln sum_j exp(s_ij)   (natural log of the scaled scores),
+ * with j ranging over all keys, or over j <= i when causal = 1.
+ *
+ * q, k, v   DEVICE pointers, [B,H,N,d] contiguous, element type `dtype`,
+ *           each 16-byte aligned. Read only.
+ * o         DEVICE pointer, [B,H,N,d] contiguous, `dtype`, 16-byte aligned;
+ *           written (rounded to nearest even from fp32 for f16/bf16).
+ * lse       DEVICE pointer, [B,H,N] fp32, 4-byte aligned; written.
+ * B, H, N   batch, heads, sequence length (queries = keys), all >= 1.
+ * d         head dimension: 64 or 128.
+ * causal    0 or 1 (1: row i attends to keys j <= i, diagonal included).
+ * scale     finite, > 0; multiplied into q.k (the usual value is 1/sqrt(d)).
+ * dtype     ATTN_F32, ATTN_F16 or ATTN_BF16. Products are accumulated in
+ *           fp32 for every dtype; f16/bf16 probabilities are rounded to the
+ *           input type before the P.V product.
+ * stream    hipStream_t to launch on (NULL = the null stream).
+ *
+ * Asynchronous: returns once the kernel is enqueued; no host synchronisation
+ * and no device allocation. The caller owns every buffer; outputs must not
+ * alias inputs. Arguments are validated before any HIP call: on an error
+ * code nothing has been launched. Inputs must be finite (NaN/Inf inputs give
+ * unspecified outputs). Calls on the same stream are ordered as usual;
+ * concurrent calls writing the same o/lse race.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+             int dtype, void* stream);
+
+/* attn_strerror — static description of a return code (never NULL). */
+const char* attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

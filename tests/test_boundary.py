@@ -1,0 +1,125 @@
+"""C-ABI boundary checks that need no GPU.
+
+* Both shared libraries load and export every function their header in
+  include/ declares.
+* attn_fwd rejects bad arguments with the documented codes. Validation runs
+  before any HIP call, so these calls never touch a device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+
+def _declared_functions(header):
+    text = open(os.path.join(INCLUDE, header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
+
+
+def _exported(lib_path):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path], check=True,
+                         capture_output=True, text=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if " T " in line}
+
+
+@pytest.fixture(scope="module")
+def attn_lib_path():
+    import exact_attention_15_amd as ea
+    if not os.path.exists(ea.LIB_PATH):
+        from exact_attention_15_amd.build import build_library
+        build_library()
+    return ea.LIB_PATH
+
+
+def test_every_header_is_covered():
+    headers = sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h"))
+    assert headers == ["attn.h", "attn_ref.h"]
+
+
+def test_attn_library_exports_header(attn_lib_path):
+    decl = _declared_functions("attn.h")
+    assert decl == ["attn_fwd", "attn_strerror"]
+    missing = set(decl) - _exported(attn_lib_path)
+    assert not missing, missing
+    ctypes.CDLL(attn_lib_path)   # loads without a GPU
+
+
+def test_oracle_library_exports_header(oracle_lib):
+    decl = _declared_functions("attn_ref.h")
+    assert decl == ["attn_fwd_ref", "attn_fwd_ref_rows", "attn_ref_decode"]
+    missing = set(decl) - _exported(oracle_lib.LIB_PATH)
+    assert not missing, missing
+
+
+def test_libraries_share_no_symbols(attn_lib_path, oracle_lib):
+    """The GPU library neither contains nor imports the oracle."""
+    gpu = _exported(attn_lib_path)
+    assert not any(s.startswith("attn_fwd_ref") or s.startswith("attn_ref") for s in gpu)
+    undef = subprocess.run(["nm", "-D", "--undefined-only", attn_lib_path], check=True,
+                           capture_output=True, text=True).stdout
+    assert "attn_fwd_ref" not in undef
+    needed = subprocess.run(["readelf", "-d", attn_lib_path], check=True,
+                            capture_output=True, text=True).stdout
+    assert "oracle" not in needed
+
+
+def test_strerror(attn_lib_path):
+    import exact_attention_15_amd as ea
+    for code in (0, -1, -2, -3, -4, 99):
+        assert isinstance(ea.strerror(code), str) and ea.strerror(code)
+
+
+def test_argument_validation(attn_lib_path):
+    """Every rejected argument returns its code before any HIP call."""
+    import exact_attention_15_amd as ea
+    # Fake, aligned "device" addresses: they are never dereferenced because
+    # each call below fails validation first.
+    P = 0x7f0000000000
+    good = dict(q=P, k=P + 0x1000, v=P + 0x2000, o=P + 0x3000, lse=P + 0x4000,
+                B=1, H=2, N=128, d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16, stream=None)
+    cases = [
+        (dict(q=None), ea.ATTN_EINVAL),
+        (dict(k=None), ea.ATTN_EINVAL),
+        (dict(v=None), ea.ATTN_EINVAL),
+        (dict(o=None), ea.ATTN_EINVAL),
+        (dict(lse=None), ea.ATTN_EINVAL),
+        (dict(B=0), ea.ATTN_EINVAL),
+        (dict(H=-1), ea.ATTN_EINVAL),
+        (dict(N=0), ea.ATTN_EINVAL),
+        (dict(N=2 ** 40), ea.ATTN_EINVAL),
+        (dict(causal=2), ea.ATTN_EINVAL),
+        (dict(scale=0.0), ea.ATTN_EINVAL),
+        (dict(scale=-1.0), ea.ATTN_EINVAL),
+        (dict(scale=float("inf")), ea.ATTN_EINVAL),
+        (dict(scale=float("nan")), ea.ATTN_EINVAL),
+        (dict(dtype=3), ea.ATTN_EINVAL),
+        (dict(d=32), ea.ATTN_EUNSUPPORTED),
+        (dict(d=96), ea.ATTN_EUNSUPPORTED),
+        (dict(q=P + 8), ea.ATTN_EALIGN),
+        (dict(o=P + 0x3002), ea.ATTN_EALIGN),
+        (dict(lse=P + 0x4002), ea.ATTN_EALIGN),
+    ]
+    for change, want in cases:
+        a = dict(good, **change)
+        rc = ea.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                         a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+        assert rc == want, (change, rc)
+
+
+def test_python_wrapper_checks(attn_lib_path):
+    import torch
+    import exact_attention_15_amd as ea
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        ea.fwd(q, q, q)   # host tensors are refused before any call
+    with pytest.raises(TypeError):
+        ea.dtype_code(torch.float64)
+    assert ea.default_scale(64) == 0.125
+    assert abs(ea.default_scale(128) - 128 ** -0.5) < 1e-8

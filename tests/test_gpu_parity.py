@@ -1,0 +1,162 @@
+"""GPU parity: the HIP path against the CPU fp64 oracle, through the C ABI.
+
+Bars (max-abs over every compared element, oracle run on the same rounded
+inputs):
+  O    fp32 <= 1e-4, fp16/bf16 <= 2e-2
+  lse  fp32 <= 1e-4, fp16 <= 5e-4, bf16 <= 2.5e-3
+The lse bounds follow from the arithmetic: the kernels sum the probabilities
+after rounding them to the P.V operand type, so ln(l) carries at most that
+type's relative half-ulp (2^-9 for bf16, 2^-12 for fp16) plus fp32 terms.
+
+Small shapes are checked element by element on every output; the full-size
+workloads (in the launch configuration the bench times) are checked on
+sampled rows the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_15_amd.inputs import WORKLOADS, make_qkv, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = {torch.float32: 1e-4, torch.float16: 2e-2, torch.bfloat16: 2e-2}
+LSE_TOL = {torch.float32: 1e-4, torch.float16: 5e-4, torch.bfloat16: 2.5e-3}
+
+
+@pytest.fixture(scope="module")
+def ea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_15_amd as ea
+    ea.load_library()
+    return ea
+
+
+def _run_gpu(ea, q, k, v, causal, scale):
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = ea.fwd(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.cpu().to(torch.float64).numpy(), lse.cpu().to(torch.float64).numpy()
+
+
+def _check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what):
+    err_o = np.abs(o_gpu - o_ref)
+    err_l = np.abs(lse_gpu - lse_ref)
+    assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), what
+    mo, ml = float(err_o.max()), float(err_l.max())
+    print(f"{what}: O max-abs {mo:.3e} mean-abs {float(err_o.mean()):.3e}; lse max-abs {ml:.3e}",
+          flush=True)
+    assert mo <= O_TOL[dtype], (what, mo)
+    assert ml <= LSE_TOL[dtype], (what, ml)
+
+
+SWEEP_N = [1, 2, 3, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 257]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16],
+                         ids=["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_sweep_small(ea, oracle_lib, dtype, d, causal):
+    """Every output element, N across tile edges and ragged tails."""
+    for n in SWEEP_N:
+        q, k, v = make_qkv(2, 2, n, d, dtype, seed=7000 + n + d)
+        scale = ea.default_scale(d)
+        o_ref, lse_ref = oracle_lib.attn_fwd_ref(q, k, v, causal, scale)
+        o, lse = _run_gpu(ea, q, k, v, causal, scale)
+        _check(o, lse, o_ref, lse_ref, dtype, f"N={n} d={d} {dtype} causal={causal}")
+
+
+def _sample_rows(B, H, N, rng, n_random=192):
+    BH = B * H
+    rows = set()
+    for i in list(range(min(N, 40))) + list(range(max(0, N - 40), N)):
+        rows.add(i)                          # slice 0: head and tail
+        rows.add((BH - 1) * N + i)           # last slice
+    mid = BH // 2
+    for t in (127, 128, 129, 255, 256, 1023, 1024, N // 2, N - 129, N - 128):
+        if 0 <= t < N:
+            rows.add(mid * N + t)
+    rows.update(rng.integers(0, BH * N, size=n_random).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(ea, oracle_lib, name):
+    """Full-size workloads: every row for the two fp32 cases, sampled rows
+    otherwise."""
+    w = WORKLOADS[name]
+    print(f"workload {name}: {w.describe()}", flush=True)
+    q, k, v = workload_inputs(w)
+    o, lse = _run_gpu(ea, q, k, v, w.causal, w.scale)
+    if w.B * w.H * w.N <= 32 * 1024:
+        o_ref, lse_ref = oracle_lib.attn_fwd_ref(q, k, v, w.causal, w.scale)
+        _check(o, lse, o_ref, lse_ref, w.dtype, name)
+        return
+    rows = _sample_rows(w.B, w.H, w.N, np.random.default_rng(w.seed))
+    o_ref, lse_ref = oracle_lib.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows)
+    _check(o.reshape(-1, w.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, w.dtype,
+           f"{name} ({len(rows)} sampled rows)")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],
+                         ids=["f32", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_invariants_on_gpu(ea, dtype, causal):
+    """Constant V gives that constant; Q = 0 gives the (prefix) mean of V
+    with lse = ln|J_i|; the unit-basis probe V[k][0] = 1 reads column k of
+    P, whose rows then sum to 1."""
+    B, H, N, d = 1, 2, 200, 64
+    q, k, v = make_qkv(B, H, N, d, dtype, seed=31)
+    tol = O_TOL[dtype]
+    c = 0.375
+    o, _ = _run_gpu(ea, q, k, torch.full_like(v, c), causal, 0.125)
+    assert np.abs(o - c).max() <= tol
+
+    o, lse = _run_gpu(ea, torch.zeros_like(q), k, v, causal, 0.125)
+    vv = v.to(torch.float64).numpy()
+    cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+    mean = (np.cumsum(vv, axis=2) / np.arange(1, N + 1)[:, None]) if causal else \
+        np.broadcast_to(vv.mean(axis=2, keepdims=True), vv.shape)
+    assert np.abs(o - mean).max() <= tol
+    assert np.abs(lse - np.log(cnt)).max() <= LSE_TOL[dtype]
+
+    n = 70
+    q2, k2, _ = make_qkv(1, 1, n, d, dtype, seed=32)
+    cols = []
+    for kk in range(n):
+        vb = torch.zeros(1, 1, n, d, dtype=dtype)
+        vb[0, 0, kk, 0] = 1.0
+        o, _ = _run_gpu(ea, q2, k2, vb, causal, 0.125)
+        assert np.abs(o[..., 1:]).max() == 0.0
+        cols.append(o[0, 0, :, 0])
+    p = np.stack(cols, axis=1)
+    assert np.abs(p.sum(1) - 1).max() <= 2 * tol
+    if causal:
+        assert np.all(p[np.triu_indices(n, 1)] == 0.0)
+
+
+def test_deterministic(ea):
+    """No atomics on the path: repeated runs are bitwise identical."""
+    w = WORKLOADS["c3_bf16_causal"]
+    q, k, v = (t.cuda() for t in make_qkv(1, 4, 1000, 64, torch.bfloat16, seed=5))
+    o1, l1 = ea.fwd(q, k, v, causal=True)
+    o2, l2 = ea.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    del w
+
+
+def test_stream_and_out_buffers(ea):
+    """Launch on a non-default stream into preallocated outputs."""
+    q, k, v = (t.cuda() for t in make_qkv(1, 2, 300, 128, torch.bfloat16, seed=6))
+    ref_o, ref_l = ea.fwd(q, k, v, causal=False)
+    s = torch.cuda.Stream()
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 2, 300, device="cuda", dtype=torch.float32)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ea.fwd(q, k, v, causal=False, out=(o, lse))
+    s.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
