@@ -26,6 +26,7 @@ FLAGS = [
     # Packed fp32 VALU forms are kept out of every kernel.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    "-Wno-inline-asm",
 ]
 
 

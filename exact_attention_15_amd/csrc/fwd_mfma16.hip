@@ -10,37 +10,53 @@
 //          exp(m_old - m_new); one reciprocal of l per row at the end;
 //     1.4 / 3.4  causal: K/V tiles wholly above the diagonal are never
 //          visited; only tiles crossing it are masked element by element;
-//     3.2  K/V tiles are double-buffered (the next tile's loads are in
-//          flight while the current one is used); keys past N are
-//          zero-filled and masked to -inf;
+//     3.2  K/V tiles are double-buffered (the next tiles' loads are in
+//          flight while the current ones are used); keys past N are masked
+//          to -inf and never meet a non-finite V value;
 //     3.3  P is computed once per tile and reused for every output column.
 //   [G7] "Flash Attention CUDA Kernel 优化: 从 56 到 986 TFLOPS on B300 —
-//          G7: 回归 1CTA", lesson 6: exp is taken as exp2 with log2(e)
-//          folded into the score scale.
-//   [naive-attn] cishoon.github.io "flashattention", 3.5: shared-memory
-//          bank conflicts are avoided by changing the layout (here an XOR
-//          swizzle of 16-byte chunks instead of padding).
+//          G7: 回归 1CTA": exp is taken as exp2 with log2(e) folded into the
+//          score scale (lesson 6); QK^T and P.V of different tiles are issued
+//          so that they interleave with the softmax (V45, V50); the rescale
+//          of the accumulator is made conditional (carried over from G6).
+//   [naive-attn] cishoon.github.io "flashattention", 3.5: shared-memory bank
+//          conflicts are removed by the layout (here XOR swizzles of 16-byte
+//          chunks instead of padding).
 //
 // gfx950 design (not the pages'):
 //   * 256 threads = 4 wave64s; each wave owns 32 query rows; the workgroup
 //     owns 128 rows. K/V tiles hold 64 keys.
-//   * Both products use v_mfma_f32_32x32x16_{bf16,f16} with fp32
+//   * Both products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32
 //     accumulation, in transposed form so that one lane owns one query:
 //        S^T[key][query] = K . Q^T     (A = K rows from LDS, B = Q in VGPRs)
 //        O^T[d][query]  += V^T . P^T   (A = V^T from LDS, B = P in VGPRs)
 //     The 32x32 accumulator gives lane l the column l%32 (its query) and 16
-//     rows (keys, or head-dim entries), so the row max / row sum of the
-//     softmax are in-lane reductions plus one exchange with lane l^32, and
-//     the per-row rescale of O is a per-lane scalar multiply.
-//   * P leaves the S^T accumulator already in the B-operand shape of the
-//     P.V product: the order of keys inside a contraction is free, so V^T is
-//     stored in LDS with its keys permuted to match (see vt_pos()).
+//     rows (keys, or head-dim entries), so the softmax row max / row sum are
+//     in-lane reductions plus one v_permlane32_swap, and the rescale of O is
+//     a per-lane scalar multiply.
+//   * P leaves the S^T accumulator already in the B-operand layout of the
+//     P.V product (the order of keys inside a contraction is free); the
+//     matching V^T operand is read from row-major V in LDS with
+//     ds_read_b64_tr_b16, two reads per MFMA.
+//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4,
+//     16 bytes per lane, no VGPR staging); the XOR swizzle is applied by
+//     choosing which global chunk each lane fetches.
+//   * Software pipeline inside each wave: iteration j issues the MFMAs of
+//     S(j+1) = K(j+1) Q^T and of O += P(j-1) V(j-1), neither of which depends
+//     on the softmax of tile j that runs on the VALU in the same iteration,
+//     so matrix and vector work overlap without relying on other waves.
+//   * Lazy rescale: the exponent base m only moves when a tile's row max
+//     exceeds it by more than 2^8 in probability; otherwise P <= 256 is used
+//     as is. The final O / l is unchanged by the choice of base, and a
+//     bf16/fp16 P keeps its relative precision at that magnitude.
 //   * Work items (b*H+h, query tile) are dispatched longest-first for causal
-//     inputs, and consecutive workgroup ids map to different (b,h) slices so
-//     that, with the round-robin placement of workgroups over the 8 XCDs,
-//     every workgroup of one slice runs on the same XCD and shares its L2.
+//     inputs; consecutive workgroup ids map to different (b,h) slices so,
+//     with the round-robin placement of workgroups over the 8 XCDs, all
+//     workgroups of one slice share one XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_internal.h"
 
@@ -54,8 +70,23 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kRescaleThreshold = 8.0f;   // log2 units: P may reach 2^8
+constexpr int kBlockN = 64;                 // keys per K/V tile
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+#ifndef ATTN_PINGPONG
+#define ATTN_PINGPONG 1
+#endif
+
+#ifndef ATTN_WAVES_PER_SIMD
+#define ATTN_WAVES_PER_SIMD 1
+#endif
 
 template <bool IS_BF16> struct Op16;
 
@@ -71,7 +102,7 @@ template <> struct Op16<true> {
         v[1] = (__bf16)y;
         return __builtin_bit_cast(uint32_t, v);
     }
-    // acc + (both packed values): sums exactly what the P.V product consumes.
+    // acc + both packed values: sums exactly what the P.V product consumes.
     static __device__ __forceinline__ float sum2(uint32_t pk, float acc) {
         const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
         return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
@@ -95,51 +126,113 @@ template <> struct Op16<false> {
     }
 };
 
-constexpr int kBlockN = 64;   // keys per K/V tile
-constexpr int kThreads = 256;
-
-// Position of key `k` (0..63 inside a tile) in a V^T row. Bits 2 and 3 of the
-// key index are swapped, so that the 8 keys one lane contributes to one
-// 32x32x16 P.V step (keys 16a + 8b + 4g + e for b in {0,1}, e in 0..3, where
-// g = lane/32) sit in 8 consecutive positions: one 16-byte LDS read.
-__device__ __forceinline__ int vt_pos(int k) {
-    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
-template <int D>
-struct Smem {
-    static constexpr int kRowBytes = D * 2;             // one K row
-    static constexpr int kTileBytes = kBlockN * D * 2;  // one K tile == one V^T tile
-    static constexpr int kVtRowBytes = kBlockN * 2;     // one V^T row (64 keys)
-    static constexpr int kBytes = 4 * kTileBytes;       // K[2] + V^T[2]
+// LDS layout of one K or V tile: 64 rows of D 16-bit values, row-major, with
+// 16-byte chunk c of row r stored at chunk c ^ swz(r).
+//  * K is read 16 bytes per lane, one row per lane, 16 lanes per LDS cycle:
+//    rows r..r+15 at one logical chunk must land in 16 different 16-byte bank
+//    groups (64 banks x 4 bytes).
+//  * V is read with ds_read_b64_tr_b16: 32 lanes read 4 consecutive rows x
+//    64 contiguous bytes; rows 2 apart (D = 64) or adjacent rows (D = 128)
+//    would otherwise share banks.
+template <int D, int WAVES = kWaves>
+struct Tile {
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kChunks = D / 8;             // 16-byte chunks per row
+    static constexpr int kBytes = kBlockN * kRowBytes;
+    static constexpr int kLoadsPerWave = kBytes / 1024 / WAVES;    // 1 KiB per wave load
+    static __device__ __forceinline__ int swz_k(int r) { return D == 64 ? (r >> 1) & 7 : r & 15; }
+    static __device__ __forceinline__ int swz_v(int r) { return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2; }
 };
 
-// Byte offset of 16-byte chunk c of K row r: chunk index XOR (r mod 8), so the
-// 8 lanes that read the same logical chunk of 8 consecutive rows hit 8
-// different bank groups.
-template <int D>
-__device__ __forceinline__ int k_off(int r, int c) {
-    return r * Smem<D>::kRowBytes + ((c ^ (r & 7)) << 4);
+// Per-lane byte offsets, inside a tile, of the 16-byte global chunks this
+// lane copies: load u of wave `wave` fills LDS chunk slots
+// s = (wave*U + u)*64 + lane, i.e. row s / kChunks, physical chunk
+// s % kChunks, holding the global chunk (physical ^ swz(row)).
+template <int D, bool IS_V, int WAVES = kWaves>
+__device__ __forceinline__ void tile_src_offsets(int wave, int lane, int* off) {
+    using T = Tile<D, WAVES>;
+#pragma unroll
+    for (int u = 0; u < T::kLoadsPerWave; ++u) {
+        const int s = (wave * T::kLoadsPerWave + u) * 64 + lane;
+        const int r = s / T::kChunks;
+        const int pc = s % T::kChunks;
+        const int lc = pc ^ (IS_V ? T::swz_v(r) : T::swz_k(r));
+        off[u] = r * T::kRowBytes + lc * 16;
+    }
 }
 
-// Byte offset of 16-byte chunk pc of V^T row dd (same swizzle).
-__device__ __forceinline__ int vt_off(int dd, int pc) {
-    return dd * (kBlockN * 2) + ((pc ^ (dd & 7)) << 4);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane HBM -> LDS copy (buffer_load_dwordx4 ... lds): lane l
+// writes LDS bytes [lds_addr + 16 l, +16). Issued from inline assembly so
+// that the compiler does not guard later LDS reads of *other* buffers with a
+// wait for the copy; every wait for these copies is explicit (vmcnt(0)
+// before the barrier that publishes a tile). The compiler's own vmcnt
+// accounting stays safe: extra outstanding loads only make its waits longer.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, int voffset) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+// Issue this wave's share of the direct HBM -> LDS copy of one K or V tile
+// (keys kv0 .. kv0+63). The buffer descriptor covers rows kv0 .. N-1 only,
+// so chunks of rows past N are out of range and arrive as zeros (the
+// zero-fill of the pages' asynchronous copy); their scores are masked.
+template <int D, int WAVES = kWaves>
+__device__ __forceinline__ void load_tile(const uint16_t* g_slice, int kv0, int N, LDS_AS char* buf,
+                                          int wave, const int* off) {
+    using T = Tile<D, WAVES>;
+    const int rows = max(N - kv0, 0);
+    const uint64_t addr = (uint64_t)(g_slice + (size_t)kv0 * D);
+    i32x4 rsrc;
+    rsrc[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    rsrc[1] = __builtin_amdgcn_readfirstlane((int)((addr >> 32) & 0xffff));   // stride 0
+    rsrc[2] = __builtin_amdgcn_readfirstlane(rows * T::kRowBytes);            // bytes in range
+    rsrc[3] = 0x00020000;                                                     // 32-bit data format
+    const uint32_t lds0 = (uint32_t)(uintptr_t)buf;
+#pragma unroll
+    for (int u = 0; u < T::kLoadsPerWave; ++u) {
+        const int slot0 = (wave * T::kLoadsPerWave + u) * 64;
+        dma16(rsrc, lds0 + slot0 * 16, off[u]);
+    }
+}
+
+__device__ __forceinline__ float wave_half_max(float x) {
+    // v_permlane32_swap(x, x): lanes < 32 get (x[l], x[l+32]), lanes >= 32 get
+    // (x[l-32], x[l]); the max of the pair is the max over lanes l and l^32.
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)r[0]),
+                                         __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float wave_half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 template <bool IS_BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, ATTN_WAVES_PER_SIMD) void fwd16_kernel(FwdParams p) {
     using Op = Op16<IS_BF16>;
-    using S = Smem<D>;
-    constexpr int KCH = D / 8;                             // 16-byte chunks per row
-    constexpr int K_ITEMS = kBlockN * KCH / kThreads;      // K chunks per thread
-    constexpr int V_ITEMS = (kBlockN / 2) * KCH / kThreads;  // (key pair, chunk) per thread
-    static_assert(K_ITEMS >= 1 && V_ITEMS >= 1, "tile / thread mismatch");
+    using T = Tile<D>;
+    constexpr int NKD = D / 16;   // QK^T contraction steps
+    constexpr int NDB = D / 32;   // 32-row blocks of O^T
 
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    // Four distinct LDS objects, so that the compiler can tell the HBM->LDS
+    // copies into one buffer from the reads of another and need not wait for
+    // the copies before those reads.
+    __shared__ __attribute__((aligned(1024))) char k_lds0[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[T::kBytes];
+    LDS_AS char* const kbuf[2] = {(LDS_AS char*)k_lds0, (LDS_AS char*)k_lds1};
+    LDS_AS char* const vbuf[2] = {(LDS_AS char*)v_lds0, (LDS_AS char*)v_lds1};
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
@@ -150,181 +243,228 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
     const int bh = w - (w / p.BH) * p.BH;
     const int N = (int)p.N;
     const int q0 = tile * kBlockM;
-    const int qi = q0 + wave * 32 + l32;   // this lane's query row
+    const int qw = q0 + wave * 32;          // first query row of this wave
+    const int qi = qw + l32;                // this lane's query row
     const size_t base = (size_t)bh * (size_t)N * D;
 
     const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + base;
     const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + base;
     const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + base;
 
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const int n_tiles = ((CAUSAL ? min(q0 + kBlockM, N) : N) + kBlockN - 1) / kBlockN;
+    // First tile that needs element masks for this wave: the first one that
+    // crosses its diagonal (causal) or N. Tiles before it are fully visible.
+    // Tile j crosses N when 64(j+1) > N, and crosses this wave's diagonal
+    // when 64j + 63 > qw.
+    int j_mask = N / kBlockN;
+    if (CAUSAL) j_mask = min(j_mask, (qw + 1) / kBlockN);
+    j_mask = min(j_mask, n_tiles);
+
+    // Prologue loads: K(0), K(1).
+    int koff_src[T::kLoadsPerWave], voff_src[T::kLoadsPerWave];
+    tile_src_offsets<D, false>(wave, lane, koff_src);
+    tile_src_offsets<D, true>(wave, lane, voff_src);
+    load_tile<D>(Kg, 0, N, kbuf[0], wave, koff_src);
+    load_tile<D>(Kg, kBlockN, N, kbuf[1], wave, koff_src);
 
     // Q fragments (B operand of S^T = K Q^T): lane holds q[qi][16kd + 8g .. +7].
-    u32x4 qf[D / 16];
+    u32x4 qf[NKD];
+    {
+        const int qrow = min(qi, N - 1);
 #pragma unroll
-    for (int kd = 0; kd < D / 16; ++kd)
-        qf[kd] = qi < N ? *(const u32x4*)(Qg + (size_t)qi * D + 16 * kd + 8 * g) : zero4;
+        for (int kd = 0; kd < NKD; ++kd)
+            qf[kd] = *(const u32x4*)(Qg + (size_t)qrow * D + 16 * kd + 8 * g);
+    }
 
-    const int kv_end = CAUSAL ? min(q0 + kBlockM, N) : N;
-    const int n_tiles = (kv_end + kBlockN - 1) / kBlockN;
-
-    // Register staging of the next K/V tile.
-    u32x4 kreg[K_ITEMS];
-    u32x4 vreg[V_ITEMS][2];
-
-    auto load_tile = [&](int kv0) {
+    // Per-lane LDS offsets of the K reads (row l32 of a 32-key block, logical
+    // chunk 2kd+g) and of the V transposed reads (see pv()).
+    int koff[NKD];
 #pragma unroll
-        for (int it = 0; it < K_ITEMS; ++it) {
-            const int item = tid + kThreads * it;
-            const int r = item / KCH, c = item % KCH;
-            const int key = kv0 + r;
-            kreg[it] = key < N ? *(const u32x4*)(Kg + (size_t)key * D + 8 * c) : zero4;
-        }
+    for (int kd = 0; kd < NKD; ++kd)
+        koff[kd] = l32 * T::kRowBytes + (((2 * kd + g) ^ T::swz_k(l32)) << 4);
+    // ds_read_b64_tr_b16: in each group of 16 lanes, output lane j receives
+    // element j%4 of the 8-byte reads of source lanes j/4 + 4k (k = 0..3).
+    // Source lane (G = lane/16, i = lane%16) therefore reads row 4g + i/4
+    // (+16kb2 + 8h) at columns 32db + 16(G%2) + 4(i%4): output lane l gets
+    // V[16kb2 + 8h + 4g + k][32db + l%32] for k = 0..3, the A operand of the
+    // P.V step with the key order of the S^T accumulator.
+    const int G = lane >> 4, i16 = lane & 15;
+    const int vrow = 4 * g + (i16 >> 2);
+    int voff[NDB];
 #pragma unroll
-        for (int it = 0; it < V_ITEMS; ++it) {
-            const int item = tid + kThreads * it;
-            const int c = item / (kBlockN / 2), pp = item % (kBlockN / 2);
-            const int key = kv0 + 2 * pp;
-            vreg[it][0] = key < N ? *(const u32x4*)(Vg + (size_t)key * D + 8 * c) : zero4;
-            vreg[it][1] = key + 1 < N ? *(const u32x4*)(Vg + (size_t)(key + 1) * D + 8 * c) : zero4;
-        }
-    };
-
-    auto store_tile = [&](int buf) {
-        char* ks = smem + buf * S::kTileBytes;
-        char* vt = smem + (2 + buf) * S::kTileBytes;
-#pragma unroll
-        for (int it = 0; it < K_ITEMS; ++it) {
-            const int item = tid + kThreads * it;
-            const int r = item / KCH, c = item % KCH;
-            *(u32x4*)(ks + k_off<D>(r, c)) = kreg[it];
-        }
-#pragma unroll
-        for (int it = 0; it < V_ITEMS; ++it) {
-            const int item = tid + kThreads * it;
-            const int c = item / (kBlockN / 2), pp = item % (kBlockN / 2);
-            const int pos = vt_pos(2 * pp);          // keys 2pp, 2pp+1 stay adjacent
-            const int pc = pos >> 3, pw = (pos & 7) * 2;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int dd = 8 * c + jj;
-                const uint32_t x = vreg[it][0][jj >> 1], y = vreg[it][1][jj >> 1];
-                const uint32_t word = (jj & 1) ? ((x >> 16) | (y & 0xffff0000u))
-                                               : ((x & 0xffffu) | (y << 16));
-                *(uint32_t*)(vt + vt_off(dd, pc) + pw) = word;
-            }
-        }
-    };
+    for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + 16 * (G & 1) + 4 * (i16 & 3);   // element column
+        const int chunk = col >> 3, half = (col >> 2) & 1;
+        voff[db] = vrow * T::kRowBytes + ((chunk ^ T::swz_v(vrow)) << 4) + half * 8;
+    }
 
     const float c2 = p.scale_log2;
-    float m_run = -INFINITY;   // running row max of the scaled (log2) scores
-    float l_run = 0.f;         // this lane's half of the running row sum
-    f32x16 o[D / 32];
+    float m_used = -INFINITY;   // exponent base (log2 domain) of P and O
+    float l_run = 0.f;          // this lane's half of the row sum
+    f32x16 o[NDB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int j = 0; j < n_tiles; ++j) {
-        const int cur = j & 1;
-        const int kv0 = j * kBlockN;
-        if (j + 1 < n_tiles) load_tile(kv0 + kBlockN);
-
-        // Causal: a tile that starts past this wave's last row contributes
-        // nothing to it (wave-uniform branch).
-        const bool wave_live = !CAUSAL || kv0 <= q0 + wave * 32 + 31;
-        if (wave_live) {
-            const char* ks = smem + cur * S::kTileBytes;
-            const char* vt = smem + (2 + cur) * S::kTileBytes;
-
-            // S^T = K Q^T for 2 blocks of 32 keys.
-            f32x16 s[2];
+    // ---- building blocks ------------------------------------------------
+    auto qk = [&](const LDS_AS char* kb_base, f32x16* s_out) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-                const int r = 32 * kb + l32;
-#pragma unroll
-                for (int kd = 0; kd < D / 16; ++kd) {
-                    const u32x4 a = *(const u32x4*)(ks + k_off<D>(r, 2 * kd + g));
-                    s[kb] = Op::mfma(a, qf[kd], s[kb]);
-                }
-            }
-
-            // Element masks only on tiles that cross the diagonal or N.
-            const bool diag = CAUSAL && (kv0 + kBlockN - 1 > q0);
-            const bool tail = kv0 + kBlockN > N;
-            if (diag || tail) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kv0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-                        const bool dead = key >= N || (CAUSAL && key > qi);
-                        if (dead) s[kb][i] = -INFINITY;
-                    }
-            }
-
-            // Online softmax in the log2 domain.
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx * c2);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-
-            uint32_t pk[2][8];
-            float lsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c2, -m_use));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][i + 1], c2, -m_use));
-                    pk[kb][i >> 1] = Op::pack2(p0, p1);
-                    lsum = Op::sum2(pk[kb][i >> 1], lsum);
-                }
-            l_run = alpha * l_run + lsum;
-            m_run = m_new;
-
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-
-            // O^T += V^T P^T, four steps of 16 keys per 32 head-dim rows.
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int rr = 32 * db + l32;
-#pragma unroll
-                for (int kb2 = 0; kb2 < 4; ++kb2) {
-                    const u32x4 a = *(const u32x4*)(vt + vt_off(rr, 2 * kb2 + g));
-                    const int h = 4 * (kb2 & 1);
-                    const u32x4 b = {pk[kb2 >> 1][h], pk[kb2 >> 1][h + 1],
-                                     pk[kb2 >> 1][h + 2], pk[kb2 >> 1][h + 3]};
-                    o[db] = Op::mfma(a, b, o[db]);
-                }
+            for (int kd = 0; kd < NKD; ++kd) {
+                const u32x4 a = *(const LDS_AS u32x4*)(kb_base + koff[kd] + kb * 32 * T::kRowBytes);
+                s_out[kb] = Op::mfma(a, qf[kd], kd == 0 ? f32x16{} : s_out[kb]);
             }
         }
+    };
 
-        if (j + 1 < n_tiles) store_tile(cur ^ 1);
+    auto pv = [&](const LDS_AS char* vb_base, const u32x4* p_in) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 4; ++kb2) {
+                const LDS_AS char* a0 = vb_base + voff[db] + (16 * kb2) * T::kRowBytes;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * T::kRowBytes));
+                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+                const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+                o[db] = Op::mfma(a, p_in[kb2], o[db]);
+            }
+        }
+    };
+
+    // Masks on tile j (keys kv0..kv0+63): the key index inside the tile of
+    // accumulator entry (kb, i) is 32kb + 8(i/4) + 4g + i%4; it is dead past
+    // `lim`. A tile past this wave's rows is thereby fully dead (P = 0).
+    auto apply_mask = [&](f32x16* s, int kv0) __attribute__((always_inline)) {
+        const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - kv0 - 4 * g;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                s[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) > lim) ? -INFINITY : s[kb][i];
+    };
+
+    // Online softmax of one S^T tile: P packed for the P.V product, l updated,
+    // and alpha (the factor O must be multiplied by) when the base moved.
+    auto softmax = [&](const f32x16* s, u32x4* p_out, float& alpha) __attribute__((always_inline)) -> bool {
+        // v_maximum3_f32: two entries per instruction (inputs are finite or
+        // -inf, so its NaN propagation never matters).
+        float mx = __builtin_elementwise_maximum(s[0][0], s[0][1]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2)
+                mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[kb][i], s[kb][i + 1]));
+        mx = wave_half_max(mx) * c2;
+        const bool need = mx > m_used + kRescaleThreshold;
+        const float m_new = need ? mx : m_used;
+        alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.f;
+        m_used = m_new;
+        const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // entries 8(kb2%2) + 2e, +1 of S block kb2/2
+                const int i = 8 * (kb2 & 1) + 2 * e;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb2 >> 1][i], c2, -m_sub));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb2 >> 1][i + 1], c2, -m_sub));
+                p_out[kb2][e] = Op::pack2(p0, p1);
+                lsum = Op::sum2(p_out[kb2][e], lsum);
+            }
+        }
+        l_run = alpha * l_run + lsum;
+        return __builtin_amdgcn_ballot_w64(need) != 0;
+    };
+
+    auto rescale_o = [&](float alpha) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    };
+
+    // ---- pipeline --------------------------------------------------------
+    // Iteration j (parity PAR = j & 1):
+    //   wait for this lane's copies; barrier;
+    //   issue copies K(j+2) -> kbuf[PAR], V(j) -> vbuf[PAR];
+    //   MFMA: S(j+1) = K(j+1) Q^T from kbuf[1-PAR]; O += P(j-1) V(j-1) from vbuf[1-PAR];
+    //   VALU: softmax of S(j) -> P(j);  then O *= alpha(j) if the base moved.
+    // Copies past the last tile read clamped rows into buffers nobody reads.
+    f32x16 sa[2], sb[2];
+    u32x4 pa[4], pb[4];
+
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this lane's prologue copies
+    __syncthreads();
+    qk(kbuf[0], sa);
+
+    // Steady state: no masks, every product needed; one basic block, so the
+    // scheduler can interleave the MFMAs with the softmax.
+    auto body_main = [&](int j, auto par_tag, f32x16* s_cur, f32x16* s_next, const u32x4* p_prev,
+                         u32x4* p_cur) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_tag)::value;
+        __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();
+        load_tile<D>(Kg, (j + 2) * kBlockN, N, kbuf[PAR], wave, koff_src);
+        load_tile<D>(Vg, j * kBlockN, N, vbuf[PAR], wave, voff_src);
+        qk(kbuf[1 - PAR], s_next);
+        pv(vbuf[1 - PAR], p_prev);
+        float alpha;
+        const bool rescale = softmax(s_cur, p_cur, alpha);
+        if (rescale) rescale_o(alpha);
+    };
+    // First, diagonal, tail and dead tiles: the general form.
+    auto body_edge = [&](int j, auto par_tag, f32x16* s_cur, f32x16* s_next, const u32x4* p_prev,
+                         u32x4* p_cur) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_tag)::value;
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();
+        load_tile<D>(Kg, (j + 2) * kBlockN, N, kbuf[PAR], wave, koff_src);
+        load_tile<D>(Vg, j * kBlockN, N, vbuf[PAR], wave, voff_src);
+        if (j + 1 < n_tiles) qk(kbuf[1 - PAR], s_next);
+        if (j >= 1) pv(vbuf[1 - PAR], p_prev);
+        if (j >= j_mask) apply_mask(s_cur, j * kBlockN);
+        float alpha;
+        const bool rescale = softmax(s_cur, p_cur, alpha);
+        if (rescale) rescale_o(alpha);
+    };
+
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // j = 0 is always an edge iteration (no P.V yet).
+    body_edge(0, P0{}, sa, sb, pb, pa);
+    int j = 1;
+    // Main iterations need j + 1 < n_tiles and j < j_mask; pairs keep the
+    // register roles static (odd j: S in sb, P into pb).
+    const int j_main_end = min(j_mask, n_tiles - 1);
+    for (; j + 1 < j_main_end; j += 2) {
+        body_main(j, P1{}, sb, sa, pa, pb);
+        body_main(j + 1, P0{}, sa, sb, pb, pa);
+    }
+    for (; j < n_tiles; j += 2) {
+        if (j < j_main_end) body_main(j, P1{}, sb, sa, pa, pb);
+        else body_edge(j, P1{}, sb, sa, pa, pb);
+        if (j + 1 < n_tiles) body_edge(j + 1, P0{}, sa, sb, pb, pa);
+    }
+    // Last P.V: P(n_tiles-1) with V(n_tiles-1), copied by the last iteration.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    {
+        const int last = n_tiles - 1;
+        if (last & 1) pv(vbuf[1], pb);
+        else pv(vbuf[0], pa);
     }
 
     // Epilogue: O = O~ / l, rounded once to the output type; lse in fp32.
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = wave_half_sum(l_run);
     const float inv = 1.f / l_tot;
     if (qi < N) {
         uint16_t* Og = (uint16_t*)p.o + base + (size_t)qi * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int dd = 32 * db + 8 * i4 + 4 * g;
@@ -332,15 +472,260 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
                                   Op::pack2(o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv)};
                 *(u32x2*)(Og + dd) = wv;
             }
-        if (g == 0) p.lse[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * kLn2;
+        if (g == 0) p.lse[(size_t)bh * N + qi] = (m_used + log2f(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong variant (the default): 512 threads = 8 wave64s, 32 query rows
+// each (256 rows per workgroup). Waves w and w+4 share one SIMD; waves 0-3
+// (group A) and 4-7 (group B) run the same per-tile sequence
+//    MFMA step j : S(j) = K(j) Q^T  and  O += P(j-1) V(j-1)
+//    VALU step j : softmax of S(j) -> P(j), rescale of O when needed
+// with a workgroup barrier after every step, group B one step behind
+// group A. Between two barriers one wave of each SIMD feeds the matrix core
+// while the other keeps the vector ALU busy. Group A copies K(j+1) and V(j)
+// HBM -> LDS at the start of its MFMA step j, into the buffers of K(j-1) and
+// V(j-2), and waits for them before the barrier that ends its VALU step j.
+constexpr int kPPThreads = 512;
+constexpr int kPPWaves = kPPThreads / 64;
+constexpr int kPPBlockM = kPPWaves * 32;
+
+template <bool IS_BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(kPPThreads, 1) void fwd16_pp_kernel(FwdParams p) {
+    using Op = Op16<IS_BF16>;
+    using T = Tile<D, kPPWaves>;
+    constexpr int NKD = D / 16;
+    constexpr int NDB = D / 32;
+
+    __shared__ __attribute__((aligned(1024))) char k_lds0[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[T::kBytes];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;              // 0: leads, 1: one phase behind
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+
+    const int w = blockIdx.x;
+    const int tile = p.n_qtiles - 1 - w / p.BH;
+    const int bh = w - (w / p.BH) * p.BH;
+    const int N = (int)p.N;
+    const int q0 = tile * kPPBlockM;
+    const int qw = q0 + wave * 32;
+    const int qi = qw + l32;
+    const size_t base = (size_t)bh * (size_t)N * D;
+
+    const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + base;
+    const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + base;
+    const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + base;
+
+    const int n_tiles = ((CAUSAL ? min(q0 + kPPBlockM, N) : N) + kBlockN - 1) / kBlockN;
+    const int n_live = CAUSAL ? min(n_tiles, (qw + 31) / kBlockN + 1) : n_tiles;
+    int j_mask = N / kBlockN;
+    if (CAUSAL) j_mask = min(j_mask, (qw + 1) / kBlockN);
+
+    // Copies are issued by the four waves of group A only.
+    int koff_src[Tile<D, 4>::kLoadsPerWave], voff_src[Tile<D, 4>::kLoadsPerWave];
+    tile_src_offsets<D, false, 4>(wave & 3, lane, koff_src);
+    tile_src_offsets<D, true, 4>(wave & 3, lane, voff_src);
+    if (grp == 0) load_tile<D, 4>(Kg, 0, N, (LDS_AS char*)k_lds0, wave, koff_src);
+
+    u32x4 qf[NKD];
+    {
+        const int qrow = min(qi, N - 1);
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd)
+            qf[kd] = *(const u32x4*)(Qg + (size_t)qrow * D + 16 * kd + 8 * g);
+    }
+
+    int koff[NKD];
+#pragma unroll
+    for (int kd = 0; kd < NKD; ++kd)
+        koff[kd] = l32 * T::kRowBytes + (((2 * kd + g) ^ T::swz_k(l32)) << 4);
+    const int G = lane >> 4, i16 = lane & 15;
+    const int vrow = 4 * g + (i16 >> 2);
+    int voff[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + 16 * (G & 1) + 4 * (i16 & 3);
+        const int chunk = col >> 3, half = (col >> 2) & 1;
+        voff[db] = vrow * T::kRowBytes + ((chunk ^ T::swz_v(vrow)) << 4) + half * 8;
+    }
+
+    const float c2 = p.scale_log2;
+    float m_used = -INFINITY;
+    float l_run = 0.f;
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    f32x16 s[2];
+    u32x4 pk[4];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) pk[kb2] = u32x4{0u, 0u, 0u, 0u};
+
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+
+    // MFMA step of tile jj: S(jj) = K(jj) Q^T, and O += P(jj-1) V(jj-1) when
+    // HAS_PV. K(jj) sits in k_lds[jj&1], V(jj-1) in v_lds[(jj-1)&1]: KPAR = jj&1.
+    auto mfma_step = [&](int jj, auto kpar_tag, auto has_pv_tag) __attribute__((always_inline)) {
+        constexpr int KPAR = decltype(kpar_tag)::value;
+        constexpr bool HAS_PV = decltype(has_pv_tag)::value;
+        const LDS_AS char* kb_base = (const LDS_AS char*)(KPAR ? k_lds1 : k_lds0);
+        const LDS_AS char* vb_base = (const LDS_AS char*)(KPAR ? v_lds0 : v_lds1);
+        // S is computed for every tile, also ones this wave does not need
+        // (their S is never read): a conditional S would cost register copies.
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd) {
+                const u32x4 a = *(const LDS_AS u32x4*)(kb_base + koff[kd] + kb * 32 * T::kRowBytes);
+                s[kb] = Op::mfma(a, qf[kd], kd == 0 ? f32x16{} : s[kb]);
+            }
+        // P of a tile past this wave's rows is all zero, so its P.V is skipped.
+        if (HAS_PV && jj - 1 < n_live) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 4; ++kb2) {
+                    const LDS_AS char* a0 = vb_base + voff[db] + (16 * kb2) * T::kRowBytes;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * T::kRowBytes));
+                    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[db] = Op::mfma(a, pk[kb2], o[db]);
+                }
+        }
+    };
+
+    // VALU step of tile jj: online softmax of S(jj) into P, rescale of O.
+    auto valu_step = [&](int jj) __attribute__((always_inline)) {
+        if (jj >= n_live) return;
+        const int kv0 = jj * kBlockN;
+        if (jj >= j_mask) {
+            const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - kv0 - 4 * g;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) > lim) ? -INFINITY : s[kb][i];
+        }
+        float mx = __builtin_elementwise_maximum(s[0][0], s[0][1]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2)
+                mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[kb][i], s[kb][i + 1]));
+        mx = wave_half_max(mx) * c2;
+        const bool need = mx > m_used + kRescaleThreshold;
+        const float m_new = need ? mx : m_used;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.f;
+        m_used = m_new;
+        const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 8 * (kb2 & 1) + 2 * e;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb2 >> 1][i], c2, -m_sub));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb2 >> 1][i + 1], c2, -m_sub));
+                pk[kb2][e] = Op::pack2(p0, p1);
+                lsum = Op::sum2(pk[kb2][e], lsum);
+            }
+        l_run = alpha * l_run + lsum;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+    };
+
+    // Workgroup barrier without a memory fence: the LDS reads of a phase are
+    // consumed by its MFMAs before the wave gets here, and the copies are
+    // waited for explicitly, so a fence would only expose HBM latency.
+    auto barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // Group A issues all copies, at the start of its MFMA step of tile j:
+    // K(j+1) -> k_lds[(j+1)&1], V(j) -> v_lds[j&1].
+    auto copies = [&](int j, auto par_tag) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_tag)::value;   // j & 1
+        if (grp == 0) {
+            if (j + 1 < n_tiles)
+                load_tile<D, 4>(Kg, (j + 1) * kBlockN, N, (LDS_AS char*)(PAR ? k_lds0 : k_lds1), wave, koff_src);
+            load_tile<D, 4>(Vg, j * kBlockN, N, (LDS_AS char*)(PAR ? v_lds1 : v_lds0), wave, voff_src);
+        }
+    };
+    // One tile: MFMA phase, barrier, VALU phase, barrier (group A first waits
+    // for its copies, which the next phase reads).
+    auto tile_steps = [&](int j, auto par_tag, auto has_pv_tag) __attribute__((always_inline)) {
+        copies(j, par_tag);
+        mfma_step(j, par_tag, has_pv_tag);
+        barrier();
+        valu_step(j);
+        if (grp == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+        barrier();
+    };
+
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using NoPV = std::integral_constant<bool, false>;
+    using WithPV = std::integral_constant<bool, true>;
+
+    // Group B runs one phase behind group A.
+    if (grp == 1) barrier();
+    tile_steps(0, P0{}, NoPV{});
+    int j = 1;
+    for (; j + 1 < n_tiles; j += 2) {
+        tile_steps(j, P1{}, WithPV{});
+        tile_steps(j + 1, P0{}, WithPV{});
+    }
+    if (j < n_tiles) {
+        tile_steps(j, P1{}, WithPV{});
+        ++j;
+    }
+    // Final P.V of tile n_tiles-1 (the S computed alongside is unused).
+    if (n_tiles & 1) mfma_step(n_tiles, P1{}, WithPV{});
+    else mfma_step(n_tiles, P0{}, WithPV{});
+    if (grp == 0) barrier();
+
+    const float l_tot = wave_half_sum(l_run);
+    const float inv = 1.f / l_tot;
+    if (qi < N) {
+        uint16_t* Og = (uint16_t*)p.o + base + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int dd = 32 * db + 8 * i4 + 4 * g;
+                const u32x2 wv = {Op::pack2(o[db][4 * i4] * inv, o[db][4 * i4 + 1] * inv),
+                                  Op::pack2(o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv)};
+                *(u32x2*)(Og + dd) = wv;
+            }
+        if (g == 0) p.lse[(size_t)bh * N + qi] = (m_used + log2f(l_tot)) * kLn2;
     }
 }
 
 template <bool IS_BF16, int D, bool CAUSAL>
-hipError_t launch(const FwdParams& p, hipStream_t s) {
+hipError_t launch(FwdParams p, hipStream_t s) {
+#if ATTN_PINGPONG
+    p.n_qtiles = (int)((p.N + kPPBlockM - 1) / kPPBlockM);
     const dim3 grid((unsigned)(p.n_qtiles * p.BH));
-    hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL>), grid, dim3(kThreads),
-                       Smem<D>::kBytes, s, p);
+    hipLaunchKernelGGL((fwd16_pp_kernel<IS_BF16, D, CAUSAL>), grid, dim3(kPPThreads), 0, s, p);
+#else
+    p.n_qtiles = (int)((p.N + kBlockM - 1) / kBlockM);
+    const dim3 grid((unsigned)(p.n_qtiles * p.BH));
+    hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL>), grid, dim3(kThreads), 0, s, p);
+#endif
     return hipGetLastError();
 }
 
