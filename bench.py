@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0
 
 DTYPE_NAME = {"torch.bfloat16": "bf16", "torch.float16": "fp16", "torch.float32": "fp32"}
 
-COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_counters.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_counters.txt")
 KERNEL_SOURCES = ["exact_attention_15_amd/csrc/fwd_mfma16.hip",
                   "exact_attention_15_amd/csrc/fwd_f32.hip",
                   "exact_attention_15_amd/csrc/attn_api.hip",
@@ -95,6 +95,9 @@ def main():
                     help="(b,h) slices the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity gate")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (the reference kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -105,6 +108,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(256 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "launches": 3}))
+        return
 
     import exact_attention_15_amd as ea
     from exact_attention_15_amd.inputs import HEADLINE, WORKLOADS, workload_inputs

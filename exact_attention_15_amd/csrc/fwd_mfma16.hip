@@ -80,6 +80,18 @@ constexpr int kBlockN = 64;                 // keys per K/V tile
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+#ifndef ATTN_L_MFMA
+#define ATTN_L_MFMA 0
+#endif
+
+#ifndef ATTN_MFMA_PREFETCH
+#define ATTN_MFMA_PREFETCH 0
+#endif
+
+#ifndef ATTN_PP_MODE
+#define ATTN_PP_MODE 0
+#endif
+
 #ifndef ATTN_PINGPONG
 #define ATTN_PINGPONG 1
 #endif
@@ -568,6 +580,11 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd16_pp_kernel(FwdParams p) {
     u32x4 pk[4];
 #pragma unroll
     for (int kb2 = 0; kb2 < 4; ++kb2) pk[kb2] = u32x4{0u, 0u, 0u, 0u};
+#if ATTN_L_MFMA
+    f32x16 lacc = {};
+    const uint32_t one2 = IS_BF16 ? 0x3f803f80u : 0x3c003c00u;   // two 1.0 in bf16 / fp16
+    const u32x4 kOnes = {one2, one2, one2, one2};
+#endif
 
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
@@ -579,6 +596,57 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd16_pp_kernel(FwdParams p) {
         constexpr bool HAS_PV = decltype(has_pv_tag)::value;
         const LDS_AS char* kb_base = (const LDS_AS char*)(KPAR ? k_lds1 : k_lds0);
         const LDS_AS char* vb_base = (const LDS_AS char*)(KPAR ? v_lds0 : v_lds1);
+#if ATTN_MFMA_PREFETCH
+        // LDS operand reads are issued ahead of the MFMAs that use them, so
+        // their latency overlaps: all K fragments and the first VPRE blocks
+        // of V^T fragments up front, the rest behind the S(jj) MFMAs.
+        constexpr int VPRE = NDB < 2 ? NDB : 2;
+        auto read_v = [&](int db, int kb2) __attribute__((always_inline)) -> u32x4 {
+            const LDS_AS char* a0 = vb_base + voff[db] + (16 * kb2) * T::kRowBytes;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * T::kRowBytes));
+            return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        u32x4 kf[2][NKD];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd)
+                kf[kb][kd] = *(const LDS_AS u32x4*)(kb_base + koff[kd] + kb * 32 * T::kRowBytes);
+        // P of a tile past this wave's rows is all zero, so its P.V is skipped.
+        const bool do_pv = HAS_PV && jj - 1 < n_live;
+        u32x4 vf[NDB][4];
+        if (do_pv) {
+#pragma unroll
+            for (int db = 0; db < VPRE; ++db)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 4; ++kb2) vf[db][kb2] = read_v(db, kb2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // S is computed for every tile, also ones this wave does not need
+        // (their S is never read): a conditional S would cost register copies.
+#pragma unroll
+        for (int kd = 0; kd < NKD; ++kd)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                s[kb] = Op::mfma(kf[kb][kd], qf[kd], kd == 0 ? f32x16{} : s[kb]);
+        if (do_pv) {
+#pragma unroll
+            for (int db = VPRE; db < NDB; ++db)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 4; ++kb2) vf[db][kb2] = read_v(db, kb2);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 4; ++kb2) o[db] = Op::mfma(vf[db][kb2], pk[kb2], o[db]);
+#if ATTN_L_MFMA
+            // Row sums of P on the matrix core: an all-ones A operand makes
+            // every row of the 32x32 result the column sums of P^T.
+#pragma unroll
+            for (int kb2 = 0; kb2 < 4; ++kb2) lacc = Op::mfma(kOnes, pk[kb2], lacc);
+#endif
+        }
+#else
         // S is computed for every tile, also ones this wave does not need
         // (their S is never read): a conditional S would cost register copies.
 #pragma unroll
@@ -600,7 +668,14 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd16_pp_kernel(FwdParams p) {
                     const u32x4 a = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     o[db] = Op::mfma(a, pk[kb2], o[db]);
                 }
+#if ATTN_L_MFMA
+            // Row sums of P on the matrix core: an all-ones A operand makes
+            // every row of the 32x32 result the column sums of P^T.
+#pragma unroll
+            for (int kb2 = 0; kb2 < 4; ++kb2) lacc = Op::mfma(kOnes, pk[kb2], lacc);
+#endif
         }
+#endif
     };
 
     // VALU step of tile jj: online softmax of S(jj) into P, rescale of O.
@@ -627,7 +702,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd16_pp_kernel(FwdParams p) {
         const float alpha = need ? __builtin_amdgcn_exp2f(m_used - m_new) : 1.f;
         m_used = m_new;
         const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-        float lsum = 0.f;
+        float lpart[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb2 = 0; kb2 < 4; ++kb2)
 #pragma unroll
@@ -636,14 +711,26 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd16_pp_kernel(FwdParams p) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb2 >> 1][i], c2, -m_sub));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb2 >> 1][i + 1], c2, -m_sub));
                 pk[kb2][e] = Op::pack2(p0, p1);
-                lsum = Op::sum2(pk[kb2][e], lsum);
+#if !ATTN_L_MFMA
+                // fp32 adds: v_dot2 would run on the matrix pipe and stall
+                // behind the other wave's MFMAs.
+                lpart[e] += p0 + p1;
+#endif
             }
-        l_run = alpha * l_run + lsum;
+#if ATTN_L_MFMA
+        (void)lpart;
+#else
+        l_run = alpha * l_run + ((lpart[0] + lpart[1]) + (lpart[2] + lpart[3]));
+#endif
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+#if ATTN_L_MFMA
+#pragma unroll
+            for (int i = 0; i < 16; ++i) lacc[i] *= alpha;
+#endif
         }
     };
 
@@ -665,6 +752,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd16_pp_kernel(FwdParams p) {
             load_tile<D, 4>(Vg, j * kBlockN, N, (LDS_AS char*)(PAR ? v_lds1 : v_lds0), wave, voff_src);
         }
     };
+#if ATTN_PP_MODE == 0
     // One tile: MFMA phase, barrier, VALU phase, barrier (group A first waits
     // for its copies, which the next phase reads).
     auto tile_steps = [&](int j, auto par_tag, auto has_pv_tag) __attribute__((always_inline)) {
@@ -675,14 +763,33 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd16_pp_kernel(FwdParams p) {
         if (grp == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
         barrier();
     };
+#else
+    // One barrier per tile. Mode 1: every wave runs MFMA(j) then VALU(j).
+    // Mode 2: group B runs VALU(j-1) then MFMA(j), so inside each barrier
+    // interval the two waves of a SIMD use the two units in opposite order.
+    auto tile_steps = [&](int j, auto par_tag, auto has_pv_tag) __attribute__((always_inline)) {
+        copies(j, par_tag);
+        if (ATTN_PP_MODE == 2 && grp == 1) {
+            if (j >= 1) valu_step(j - 1);
+            mfma_step(j, par_tag, has_pv_tag);
+        } else {
+            mfma_step(j, par_tag, has_pv_tag);
+            valu_step(j);
+        }
+        if (grp == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+        barrier();
+    };
+#endif
 
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     using NoPV = std::integral_constant<bool, false>;
     using WithPV = std::integral_constant<bool, true>;
 
+#if ATTN_PP_MODE == 0
     // Group B runs one phase behind group A.
     if (grp == 1) barrier();
+#endif
     tile_steps(0, P0{}, NoPV{});
     int j = 1;
     for (; j + 1 < n_tiles; j += 2) {
@@ -693,12 +800,21 @@ __global__ __launch_bounds__(kPPThreads, 1) void fwd16_pp_kernel(FwdParams p) {
         tile_steps(j, P1{}, WithPV{});
         ++j;
     }
+#if ATTN_PP_MODE == 2
+    if (grp == 1) valu_step(n_tiles - 1);
+#endif
     // Final P.V of tile n_tiles-1 (the S computed alongside is unused).
     if (n_tiles & 1) mfma_step(n_tiles, P1{}, WithPV{});
     else mfma_step(n_tiles, P0{}, WithPV{});
+#if ATTN_PP_MODE == 0
     if (grp == 0) barrier();
+#endif
 
+#if ATTN_L_MFMA
+    const float l_tot = lacc[0];
+#else
     const float l_tot = wave_half_sum(l_run);
+#endif
     const float inv = 1.f / l_tot;
     if (qi < N) {
         uint16_t* Og = (uint16_t*)p.o + base + (size_t)qi * D;
