@@ -88,11 +88,13 @@ def cpu_baseline(w, q, k, v, n_slices: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    # The GPU needs ~1000 back-to-back launches (a few hundred ms) to reach
+    # its sustained clocks; fewer warm-up launches time a ramping clock.
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--cpu-slices", type=int, default=16,
-                    help="(b,h) slices the CPU oracle baseline runs on")
+    ap.add_argument("--cpu-slices", type=int, default=64,
+                    help="(b,h) slices the CPU oracle baseline runs on (capped at B*H)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity gate")
     ap.add_argument("--copy-calibration", action="store_true",
