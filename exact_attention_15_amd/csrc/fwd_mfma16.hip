@@ -358,6 +358,47 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
         for (int kb2 = 0; kb2 < 4; ++kb2) pk[qb][kb2] = u32x4{0u, 0u, 0u, 0u};
     }
 
+    // Row maxima and rescale decisions of the current tile. At d = 64 the
+    // VALU step is the longer of the two steps, so they are taken in the
+    // MFMA step (they need only S); at d = 128 the MFMA step is the longer
+    // one and they stay in the VALU step.
+    constexpr bool kMaxInMfmaStep = D == 64;
+    float m_old[QB];
+    bool need[QB];
+    // Scores past the causal diagonal or past N become -inf; then the row
+    // maximum and the lazy choice of the exponent base.
+    auto mask_and_max = [&](int jj) __attribute__((always_inline)) {
+        if (jj >= j_mask) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                // key index inside the tile of accumulator entry (kb, i) is
+                // 32kb + 8(i/4) + 4g + i%4; it is dead past `lim`.
+                const int qi = qw + 32 * qb + l32;
+                const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - jj * kBlockN - 4 * g;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        s[qb][kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) > lim) ? -INFINITY : s[qb][kb][i];
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            // Two chains of 3-input maxima, two entries per instruction.
+            float mxa = s[qb][0][0], mxb = s[qb][1][0];
+#pragma unroll
+            for (int i = 1; i < 15; i += 2) {
+                mxa = max3(mxa, s[qb][0][i], s[qb][0][i + 1]);
+                mxb = max3(mxb, s[qb][1][i], s[qb][1][i + 1]);
+            }
+            float mx = max3(mxa, mxb, max3(s[qb][0][15], s[qb][1][15], s[qb][1][15]));
+            mx = half_swap_max(mx) * c2;
+            m_old[qb] = m_used[qb];
+            need[qb] = mx > m_old[qb] + kRescaleThreshold;
+            m_used[qb] = need[qb] ? mx : m_old[qb];
+        }
+    };
+
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this lane's copy of K(0)
     __syncthreads();
 
@@ -422,68 +463,49 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 2);
         }
+        if (kMaxInMfmaStep && jj < n_live) mask_and_max(jj);
     };
 
-    // VALU step of tile jj for query block qb: online softmax of S(jj) into
-    // P, rescale of O when the base moves.
-    auto softmax = [&](int jj, int qb) __attribute__((always_inline)) {
-        const int qi = qw + 32 * qb + l32;
-        const int kv0 = jj * kBlockN;
-        if (jj >= j_mask) {
-            // key index inside the tile of accumulator entry (kb, i) is
-            // 32kb + 8(i/4) + 4g + i%4; it is dead past `lim`.
-            const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - kv0 - 4 * g;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    s[qb][kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) > lim) ? -INFINITY : s[qb][kb][i];
-        }
-        // Row maximum: two chains of 3-input maxima, two entries per
-        // instruction.
-        float mxa = s[qb][0][0], mxb = s[qb][1][0];
-#pragma unroll
-        for (int i = 1; i < 15; i += 2) {
-            mxa = max3(mxa, s[qb][0][i], s[qb][0][i + 1]);
-            mxb = max3(mxb, s[qb][1][i], s[qb][1][i + 1]);
-        }
-        float mx = max3(mxa, mxb, max3(s[qb][0][15], s[qb][1][15], s[qb][1][15]));
-        mx = half_swap_max(mx) * c2;
-        const float m_old = m_used[qb];
-        const bool need = mx > m_old + kRescaleThreshold;
-        const float m_new = need ? mx : m_old;
-        m_used[qb] = m_new;
-        // The base is -inf only while every score so far is masked, which
-        // takes a masked tile; it is then replaced by 0 so that the -inf
-        // scores give 0 instead of NaN.
-        const float m_sub = (jj >= j_mask && m_new == -INFINITY) ? 0.f : m_new;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 4; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // entries 8(kb2%2) + 2e, +1 of S block kb2/2
-                const int i = 8 * (kb2 & 1) + 2 * e;
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb2 >> 1][i], c2, -m_sub));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb2 >> 1][i + 1], c2, -m_sub));
-                pk[qb][kb2][e] = Op::pack2(p0, p1);
-            }
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-            // Rare: the base moved for some row of the wave.
-            const float alpha = need ? __builtin_amdgcn_exp2f(m_old - m_new) : 1.f;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha;
-            // Row-sum entries 0 / 1 belong to queries l%16 / l%16 + 16.
-            lacc[qb][0] *= alpha;
-            lacc[qb][1] *= permlane16_swap_y(alpha, alpha);
-        }
-    };
-
+    // VALU step of tile jj: online softmax of S(jj) into P for every query
+    // block, and the rescale of O where the exponent base moved. The blocks'
+    // maxima, exponentials and packing form one straight stretch of code (the
+    // rescale branches come last), so the compiler can overlap one block's
+    // maximum with the other block's exponentials: v_exp_f32, one per ~23
+    // cycles of a wave, is what bounds this step.
     auto valu_step = [&](int jj) __attribute__((always_inline)) {
         if (jj >= n_live) return;
+        if (!kMaxInMfmaStep) mask_and_max(jj);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) softmax(jj, qb);
+        for (int qb = 0; qb < QB; ++qb) {
+            // The base is -inf only while every score so far is masked, which
+            // takes a masked tile; it is then replaced by 0 so that the -inf
+            // scores give 0 instead of NaN.
+            const float m_sub = (jj >= j_mask && m_used[qb] == -INFINITY) ? 0.f : m_used[qb];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 4; ++kb2)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // entries 8(kb2%2) + 2e, +1 of S block kb2/2
+                    const int i = 8 * (kb2 & 1) + 2 * e;
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb2 >> 1][i], c2, -m_sub));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb2 >> 1][i + 1], c2, -m_sub));
+                    pk[qb][kb2][e] = Op::pack2(p0, p1);
+                }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if (__builtin_amdgcn_ballot_w64(need[qb]) != 0) {
+                // Rare: the base moved for some row of the block.
+                const float alpha = need[qb] ? __builtin_amdgcn_exp2f(m_old[qb] - m_used[qb]) : 1.f;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha;
+                // Row-sum entries 0 / 1 belong to queries l%16 / l%16 + 16.
+                lacc[qb][0] *= alpha;
+                lacc[qb][1] *= permlane16_swap_y(alpha, alpha);
+            }
+        }
     };
 
     // Workgroup barrier without a memory fence: the LDS reads of a step are
