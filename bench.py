@@ -43,9 +43,11 @@ def attention_flops(B, H, N, d, causal) -> float:
     return f / 2 if causal else f
 
 
-def algorithmic_bytes(B, H, N, d, elem_bytes) -> int:
-    """Q, K, V read once, O written once, plus the fp32 lse row statistic."""
-    return 4 * B * H * N * d * elem_bytes + 4 * B * H * N
+def algorithmic_bytes(B, H, N, d, elem_bytes, H_kv=None) -> int:
+    """Q, K, V read once, O written once, plus the fp32 lse row statistic
+    (K and V have H_kv heads under grouped-query attention)."""
+    H_kv = H if H_kv is None else H_kv
+    return 2 * B * (H + H_kv) * N * d * elem_bytes + 4 * B * H * N
 
 
 def kernel_source_hash() -> str:
@@ -171,7 +173,7 @@ def main():
     flops = attention_flops(w.B, w.H, w.N, w.d, w.causal)
     tflops = flops / (ms * 1e-3) / 1e12
     elem = 4 if dt_name == "fp32" else 2
-    abytes = algorithmic_bytes(w.B, w.H, w.N, w.d, elem)
+    abytes = algorithmic_bytes(w.B, w.H, w.N, w.d, elem, w.kv_heads)
     peak = PEAK_TFLOPS[dt_name]
     traffic = measured_traffic(name)
 
@@ -188,8 +190,9 @@ def main():
         "vs_baseline": None,
         "dtype": dt_name,
         "data": "synthetic (seeded i.i.d. N(0,1) inputs rounded to the dtype)",
-        "config": {"workload": w.describe(), "name": name, "B": w.B, "H": w.H, "N": w.N,
-                   "d": w.d, "causal": w.causal, "scale": w.scale},
+        "config": {"workload": w.describe(), "name": name, "B": w.B, "H": w.H,
+                   "H_kv": w.kv_heads, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": w.scale},
         "pct_of_peak": round(100 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),

@@ -41,6 +41,9 @@ def load_library():
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                              ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                 ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_fwd_gqa.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -71,16 +74,29 @@ def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> int:
                                    float(scale), int(dtype), stream)
 
 
+def attn_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, dtype, stream) -> int:
+    """Raw C-ABI call (grouped-query form) with integer pointers."""
+    return load_library().attn_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, int(causal),
+                                       float(scale), int(dtype), stream)
+
+
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None):
-    """O, lse = attention forward of q, k, v ([B,H,N,d] device tensors).
+    """O, lse = attention forward of q [B,H,N,d] and k, v [B,H_kv,N,d].
+
+    H_kv = H is multi-head attention; a smaller H_kv dividing H is
+    grouped-query attention (query head h reads K/V head h // (H // H_kv)),
+    H_kv = 1 multi-query attention.
 
     Returns ``o`` (same dtype/shape as q) and ``lse`` (float32 [B,H,N],
     natural-log log-sum-exp of the scaled scores). ``out`` may pass
     preallocated ``(o, lse)`` tensors.
     """
     import torch
-    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or \
+            (k.shape[0], k.shape[2], k.shape[3]) != (q.shape[0], q.shape[2], q.shape[3]):
+        raise ValueError("need q [B, H, N, d] and k, v [B, H_kv, N, d]")
+    if k.shape[1] < 1 or q.shape[1] % k.shape[1] != 0:
+        raise ValueError(f"K/V heads ({k.shape[1]}) must divide query heads ({q.shape[1]})")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
     if q.device.type != "cuda" or k.device != q.device or v.device != q.device:
@@ -89,6 +105,7 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None):
         if not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous [B, H, N, d]")
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
     if scale is None:
         scale = default_scale(d)
     if out is None:
@@ -103,12 +120,13 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None):
             raise ValueError("out[1] must be float32 [B, H, N] on q's device")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                      B, H, N, d, causal, scale, dtype_code(q.dtype), stream)
+        rc = attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          lse.data_ptr(), B, H, H_kv, N, d, causal, scale,
+                          dtype_code(q.dtype), stream)
     if rc != ATTN_OK:
         raise AttnError(rc, strerror(rc))
     return o, lse
 
 
-__all__ = ["fwd", "attn_fwd", "load_library", "strerror", "AttnError", "default_scale",
+__all__ = ["fwd", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
            "dtype_code", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -13,9 +13,11 @@
 namespace {
 
 int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale, int dtype) {
+             int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int causal, float scale,
+             int dtype) {
     if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
     if (B < 1 || H < 1 || N < 1) return ATTN_EINVAL;
+    if (H_kv < 1 || H % H_kv != 0) return ATTN_EINVAL;
     if (causal != 0 && causal != 1) return ATTN_EINVAL;
     if (!isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
@@ -32,10 +34,10 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 
 }  // namespace
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                        int dtype, void* stream) {
-    const int rc = validate(q, k, v, o, lse, B, H, N, d, causal, scale, dtype);
+extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                            int causal, float scale, int dtype, void* stream) {
+    const int rc = validate(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, dtype);
     if (rc != ATTN_OK) return rc;
 
     attn::FwdParams p;
@@ -46,6 +48,9 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     p.lse = lse;
     p.N = N;
     p.BH = (int)(B * H);
+    p.BH_kv = (int)(B * H_kv);
+    p.H_kv = (int)H_kv;
+    p.G = (int)(H / H_kv);
     p.n_qtiles = (int)((N + attn::kBlockM - 1) / attn::kBlockM);
     // scale * log2(e), rounded once to fp32: scores go straight into exp2.
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
@@ -60,10 +65,16 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                        int dtype, void* stream) {
+    return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
+}
+
 extern "C" const char* attn_strerror(int code) {
     switch (code) {
         case ATTN_OK: return "ok";
-        case ATTN_EINVAL: return "invalid argument";
+        case ATTN_EINVAL: return "invalid argument (pointer, size, H_kv, dtype, scale or causal)";
         case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128)";
         case ATTN_EALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
         case ATTN_EHIP: return "HIP kernel launch failed";

@@ -14,10 +14,32 @@ struct FwdParams {
     void* o;
     float* lse;
     int64_t N;          // sequence length (queries = keys)
-    int BH;             // B * H slices
+    int BH;             // B * H query slices
+    int BH_kv;          // B * H_kv key/value slices
+    int H_kv;           // key/value heads; H_kv divides H
+    int G;              // H / H_kv query heads per key/value head
     int n_qtiles;       // ceil(N / query-tile rows)
     float scale_log2;   // scale * log2(e): scores enter exp2 directly
 };
+
+// Slice indices of work item r in [0, BH): the (b, h) query slice and the
+// (b, h_kv) key/value slice it reads, h_kv = h / G (grouped-query attention:
+// G consecutive query heads share one K/V head). The G query heads of one K/V
+// head take the work items kv, kv + BH_kv, kv + 2 BH_kv, ...: the same
+// position modulo 8, so the same XCD and L2, whenever BH_kv is a multiple
+// of 8. With G = 1 both indices are r.
+struct SliceIds {
+    int bh;
+    int kv_bh;
+};
+
+__device__ __forceinline__ SliceIds slice_of(const FwdParams& p, int r) {
+    const int kv_bh = r % p.BH_kv;
+    const int g = r / p.BH_kv;
+    const int b = kv_bh / p.H_kv;
+    const int h = (kv_bh - b * p.H_kv) * p.G + g;
+    return {b * p.H_kv * p.G + h, kv_bh};
+}
 
 // Query rows per workgroup for every kernel here.
 constexpr int kBlockM = 128;

@@ -63,15 +63,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdParams p) {
 
     const int w = blockIdx.x;
     const int tile = p.n_qtiles - 1 - w / p.BH;
-    const int bh = w - (w / p.BH) * p.BH;
+    const SliceIds ids = slice_of(p, w - (w / p.BH) * p.BH);
+    const int bh = ids.bh;
     const int N = (int)p.N;
     const int q0 = tile * kBlockM;
     const int qi = q0 + wave * 32 + l32;
     const size_t base = (size_t)bh * (size_t)N * D;
+    const size_t kv_base = (size_t)ids.kv_bh * (size_t)N * D;
 
     const float* __restrict__ Qg = (const float*)p.q + base;
-    const float* __restrict__ Kg = (const float*)p.k + base;
-    const float* __restrict__ Vg = (const float*)p.v + base;
+    const float* __restrict__ Kg = (const float*)p.k + kv_base;
+    const float* __restrict__ Vg = (const float*)p.v + kv_base;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     // Q half-row of this lane: q[qi][g*D/2 .. g*D/2 + D/2 - 1].

@@ -269,15 +269,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
     // Work item: longest query tiles first; consecutive ids -> different slices.
     const int w = blockIdx.x;
     const int tile = p.n_qtiles - 1 - w / p.BH;
-    const int bh = w - (w / p.BH) * p.BH;
+    const SliceIds ids = slice_of(p, w - (w / p.BH) * p.BH);
+    const int bh = ids.bh;
     const int N = (int)p.N;
     const int q0 = tile * BM;
     const int qw = q0 + wave * 32 * QB;     // first query row of this wave
     const size_t base = (size_t)bh * (size_t)N * D;
+    const size_t kv_base = (size_t)ids.kv_bh * (size_t)N * D;
 
     const uint16_t* __restrict__ Qg = (const uint16_t*)p.q + base;
-    const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + base;
-    const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + base;
+    const uint16_t* __restrict__ Kg = (const uint16_t*)p.k + kv_base;
+    const uint16_t* __restrict__ Vg = (const uint16_t*)p.v + kv_base;
 
     const int n_tiles = ((CAUSAL ? min(q0 + BM, N) : N) + kBlockN - 1) / kBlockN;
     // Tiles this wave needs at all: causal tiles starting past its last row
@@ -463,7 +465,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 2);
         }
-        if (kMaxInMfmaStep && jj < n_live) mask_and_max(jj);
+        // (jj < n_tiles is implied by jj < n_live; stated, it lets the
+        // compiler drop this from the last step, whose S is never used.)
+        if (kMaxInMfmaStep && jj < n_tiles && jj < n_live) mask_and_max(jj);
     };
 
     // VALU step of tile jj: online softmax of S(jj) into P for every query

@@ -5,7 +5,8 @@ the attention arithmetic. Both the GPU path's tests/bench and the CPU oracle
 are fed from here, so they see identical bits.
 
 Recipe: Q, K, V drawn i.i.d. N(0,1) in float32 from ``torch.Generator('cpu')``
-seeded with ``seed``, in the order Q, K, V, each ``[B, H, N, d]`` contiguous;
+seeded with ``seed``, in the order Q, K, V; Q is ``[B, H, N, d]`` and K, V are
+``[B, H_kv, N, d]`` (H_kv = H unless the workload is grouped-query), contiguous;
 optionally multiplied by ``value_scale`` in float32; then rounded to the
 target dtype with round-to-nearest-even (``Tensor.to``). The unit-variance
 inputs are the setting in which the cishoon.github.io "flashattention" post,
@@ -29,6 +30,11 @@ class Workload:
     causal: bool
     value_scale: float = 1.0
     seed: int = 0
+    H_kv: int | None = None   # K/V heads (grouped-query attention); None: H
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.H_kv is None else self.H_kv
 
     @property
     def scale(self) -> float:
@@ -38,7 +44,8 @@ class Workload:
     def describe(self) -> str:
         dt = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}[self.dtype]
         c = "causal" if self.causal else "non-causal"
-        return f"{dt} {c} attention fwd B={self.B} H={self.H} N={self.N} d={self.d}"
+        kv = "" if self.H_kv is None else f" H_kv={self.H_kv}"
+        return f"{dt} {c} attention fwd B={self.B} H={self.H}{kv} N={self.N} d={self.d}"
 
 
 def _wl(cfg: int, variant: int, **kw) -> Workload:
@@ -63,19 +70,26 @@ WORKLOADS = {
                   B=1, H=8, N=16384, d=64, causal=False, value_scale=0.5),
     "c5_f16_ragged": _wl(5, 1, name="c5_f16_ragged", dtype=torch.float16,
                          B=1, H=8, N=16383, d=64, causal=False, value_scale=0.5),
+    # Grouped-query forms of the headline case (4 query heads per K/V head)
+    # and of the long d=128 case with a single K/V head (multi-query).
+    "g1_bf16_causal_gqa4": _wl(6, 0, name="g1_bf16_causal_gqa4", dtype=torch.bfloat16,
+                               B=4, H=16, H_kv=4, N=4096, d=64, causal=True),
+    "g2_bf16_d128_mqa": _wl(6, 1, name="g2_bf16_d128_mqa", dtype=torch.bfloat16,
+                            B=1, H=32, H_kv=1, N=8192, d=128, causal=True),
 }
 
 HEADLINE = "c3_bf16_causal"
 
 
 def make_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
-             value_scale: float = 1.0):
-    """Draw Q, K, V (in that order) on the CPU; return dtype tensors."""
+             value_scale: float = 1.0, H_kv: int | None = None):
+    """Draw Q [B,H,N,d], then K and V [B,H_kv,N,d] (H_kv defaults to H) on the
+    CPU; return dtype tensors."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     out = []
-    for _ in range(3):
-        x = torch.randn((B, H, N, d), dtype=torch.float32, generator=g)
+    for heads in (H, H if H_kv is None else H_kv, H if H_kv is None else H_kv):
+        x = torch.randn((B, heads, N, d), dtype=torch.float32, generator=g)
         if value_scale != 1.0:
             x = x * torch.tensor(value_scale, dtype=torch.float32)
         out.append(x.to(dtype).contiguous())
@@ -83,4 +97,4 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
 
 
 def workload_inputs(w: Workload):
-    return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.value_scale)
+    return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.value_scale, w.H_kv)

@@ -19,7 +19,8 @@
  *                 and masked), 3.5 (rows past N are not written).
  *   [FA2-principles] "Flash Attention v2 的核心优化原理与工程实现", section 4:
  *                 per-row statistics are written next to O (here folded into
- *                 one log-sum-exp per row).
+ *                 one log-sum-exp per row); References item 5: Flash
+ *                 Attention combined with grouped-query attention (GQA).
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -36,7 +37,7 @@ typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
 /* Return codes. */
 enum {
     ATTN_OK = 0,
-    ATTN_EINVAL = -1,       /* bad argument (null pointer, size, dtype, scale, causal) */
+    ATTN_EINVAL = -1,       /* bad argument (null pointer, size, H_kv, dtype, scale, causal) */
     ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128 */
     ATTN_EALIGN = -3,       /* a base pointer not 16-byte aligned */
     ATTN_EHIP = -4          /* the HIP launch failed */
@@ -75,6 +76,24 @@ enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
              int dtype, void* stream);
+
+/*
+ * attn_fwd_gqa — the same forward pass with grouped-query attention
+ * ([FA2-principles], References item 5): k and v carry H_kv heads, and query
+ * head h reads key/value head h / (H / H_kv), so groups of H / H_kv
+ * consecutive query heads share one K/V head:
+ *   s_ij = scale * q[b,h,i,:] . k[b,h/G,j,:],  o[b,h,i,:] = sum_j p_ij v[b,h/G,j,:],
+ * G = H / H_kv. H_kv = H is attn_fwd itself; H_kv = 1 is multi-query attention.
+ *
+ * q, o      [B,H,N,d] as in attn_fwd; lse [B,H,N].
+ * k, v      DEVICE pointers, [B,H_kv,N,d] contiguous, `dtype`, 16-byte aligned.
+ * H_kv      >= 1 and dividing H; otherwise ATTN_EINVAL.
+ * Everything else (types, alignment, errors, asynchrony, ownership) is as
+ * for attn_fwd.
+ */
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int causal,
+                 float scale, int dtype, void* stream);
 
 /* attn_strerror — static description of a return code (never NULL). */
 const char* attn_strerror(int code);

@@ -78,6 +78,25 @@ int attn_fwd_ref_rows(const void* q, const void* k, const void* v,
                       const int64_t* rows, int64_t n_rows,
                       double* o_rows, double* lse_rows, int num_threads);
 
+/*
+ * attn_fwd_ref_gqa / attn_fwd_ref_rows_gqa — the same with grouped-query
+ * attention ([FA2-principles], References item 5: GQA combined with Flash
+ * Attention). q and the outputs have H heads, k and v have H_kv heads,
+ * [B,H_kv,N,d] contiguous; query head h reads K/V head h / (H / H_kv).
+ * H_kv must divide H (H_kv = H: multi-head, H_kv = 1: multi-query);
+ * otherwise ATTN_REF_EINVAL. Row ids r = (b*H + h)*N + i as above.
+ * attn_fwd_ref and attn_fwd_ref_rows are these with H_kv = H.
+ */
+int attn_fwd_ref_gqa(const void* q, const void* k, const void* v,
+                     double* o_ref, double* lse_ref,
+                     int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                     int causal, float scale, int dtype, int num_threads);
+int attn_fwd_ref_rows_gqa(const void* q, const void* k, const void* v,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                          int causal, float scale, int dtype,
+                          const int64_t* rows, int64_t n_rows,
+                          double* o_rows, double* lse_rows, int num_threads);
+
 /* attn_ref_decode — widen n elements of `dtype` to double, exactly, from the
  * format definitions (sign, exponent, mantissa). Exposed so the decoder can
  * be checked against every 16-bit pattern. Returns ATTN_REF_OK or EINVAL. */

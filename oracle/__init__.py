@@ -8,7 +8,9 @@ This module is a thin ctypes loader for ``liboracle_attn.so`` (built from
 ``attn_ref.c`` by :func:`build`). The arithmetic lives entirely in the C file,
 which follows the attention definition of the cishoon.github.io
 "flashattention" post, section 1.1.2, with the causal convention of
-"Flash Attention（二）v2版本朴素实现 cuda core", section 3.4.
+"Flash Attention（二）v2版本朴素实现 cuda core", section 3.4. Grouped-query
+attention (the FlashAttention-2 principles page, References item 5) is taken
+from k/v having fewer heads than q: query head h reads K/V head h // (H // H_kv).
 """
 from __future__ import annotations
 
@@ -55,6 +57,15 @@ def _load():
                                       ctypes.POINTER(ctypes.c_int64), i64, dp, dp,
                                       ctypes.c_int]
     lib.attn_fwd_ref_rows.restype = ctypes.c_int
+    lib.attn_fwd_ref_gqa.argtypes = [vp, vp, vp, dp, dp, i64, i64, i64, i64, i64,
+                                     ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                     ctypes.c_int]
+    lib.attn_fwd_ref_gqa.restype = ctypes.c_int
+    lib.attn_fwd_ref_rows_gqa.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64,
+                                          ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_int64), i64, dp, dp,
+                                          ctypes.c_int]
+    lib.attn_fwd_ref_rows_gqa.restype = ctypes.c_int
     lib.attn_ref_decode.argtypes = [vp, dp, i64, ctypes.c_int]
     lib.attn_ref_decode.restype = ctypes.c_int
     _lib = lib
@@ -79,19 +90,30 @@ def _dptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
-def attn_fwd_ref(q, k, v, causal: bool, scale: float, num_threads: int = 0):
-    """Full oracle. q, k, v: CPU torch tensors [B,H,N,d] of one dtype.
+def _kv_heads(q, k, v) -> int:
+    B, H, N, d = q.shape
+    if k.dim() != 4 or tuple(k.shape) != tuple(v.shape) or \
+            (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d):
+        raise ValueError(f"oracle: k/v shapes {tuple(k.shape)}, {tuple(v.shape)} "
+                         f"do not fit q {tuple(q.shape)}")
+    return int(k.shape[1])
 
+
+def attn_fwd_ref(q, k, v, causal: bool, scale: float, num_threads: int = 0):
+    """Full oracle. q: CPU tensor [B,H,N,d]; k, v: [B,H_kv,N,d], one dtype.
+
+    H_kv = H is multi-head attention; H_kv < H (dividing H) is grouped-query.
     Returns (o, lse) as float64 numpy arrays of shapes [B,H,N,d] and [B,H,N].
     """
     lib = _load()
     q, k, v = _as_host(q), _as_host(k), _as_host(v)
     B, H, N, d = q.shape
+    H_kv = _kv_heads(q, k, v)
     o = np.empty((B, H, N, d), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
-    rc = lib.attn_fwd_ref(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dptr(o), _dptr(lse),
-                          B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q),
-                          int(num_threads))
+    rc = lib.attn_fwd_ref_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dptr(o),
+                              _dptr(lse), B, H, H_kv, N, d, int(bool(causal)),
+                              float(scale), _dtype_code(q), int(num_threads))
     if rc != 0:
         raise RuntimeError(f"attn_fwd_ref failed with code {rc}")
     return o, lse
@@ -105,14 +127,15 @@ def attn_fwd_ref_rows(q, k, v, causal: bool, scale: float, rows, num_threads: in
     lib = _load()
     q, k, v = _as_host(q), _as_host(k), _as_host(v)
     B, H, N, d = q.shape
+    H_kv = _kv_heads(q, k, v)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     n = rows.shape[0]
     o = np.empty((n, d), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
-    rc = lib.attn_fwd_ref_rows(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d,
-                               int(bool(causal)), float(scale), _dtype_code(q),
-                               rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
-                               _dptr(o), _dptr(lse), int(num_threads))
+    rc = lib.attn_fwd_ref_rows_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, H_kv,
+                                   N, d, int(bool(causal)), float(scale), _dtype_code(q),
+                                   rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
+                                   _dptr(o), _dptr(lse), int(num_threads))
     if rc != 0:
         raise RuntimeError(f"attn_fwd_ref_rows failed with code {rc}")
     return o, lse

@@ -22,6 +22,12 @@
  * The scale is the caller's fp32 value widened to double, so that the oracle
  * and any other implementation use the identical number.
  *
+ * Grouped-query attention ([FA2-principles], References item 5: Flash
+ * Attention combined with GQA, K/V shared by groups of query heads): with
+ * H_kv K/V heads, query head h reads K/V head h / (H / H_kv), i.e. groups of
+ * H / H_kv consecutive query heads share one K/V head. H_kv = H is ordinary
+ * multi-head attention, H_kv = 1 multi-query attention.
+ *
  * Pinned by tests/test_oracle_pins.py against closed forms, invariants the
  * pages state (rows of P sum to 1, constant V, Q = 0 mean, unit-basis probe,
  * causal row 0, N = 1 and N = 2 closed forms), brute force on tiny inputs
@@ -90,7 +96,7 @@ int attn_ref_decode(const void* src, double* dst, int64_t n, int dtype)
 
 typedef struct {
     const void *q, *k, *v;
-    int64_t B, H, N, d;
+    int64_t B, H, H_kv, N, d;
     int causal;
     double scale;
     int dtype;
@@ -110,7 +116,10 @@ static void one_row(job_t* jb, int64_t t, double* s_row, double* qrow)
     const int64_t r = jb->rows[t];
     const int64_t bh = r / N;          /* (b*H + h) */
     const int64_t i = r % N;           /* query position */
-    const int64_t slice = bh * N * d;  /* element offset of the (b,h) slice */
+    const int64_t slice = bh * N * d;  /* element offset of the (b,h) slice of q */
+    /* K/V head of query head h: h / (H / H_kv) */
+    const int64_t b = bh / jb->H, h = bh % jb->H;
+    const int64_t kv_slice = (b * jb->H_kv + h / (jb->H / jb->H_kv)) * N * d;
 
     /* visible keys: j in [0, n_vis) */
     const int64_t n_vis = jb->causal ? i + 1 : N;
@@ -122,7 +131,7 @@ static void one_row(job_t* jb, int64_t t, double* s_row, double* qrow)
     for (int64_t j = 0; j < n_vis; j++) {
         double dot = 0.0;
         for (int64_t c = 0; c < d; c++)
-            dot += qrow[c] * decode_one(jb->k, slice + j * d + c, jb->dtype);
+            dot += qrow[c] * decode_one(jb->k, kv_slice + j * d + c, jb->dtype);
         s_row[j] = jb->scale * dot;
     }
 
@@ -146,7 +155,7 @@ static void one_row(job_t* jb, int64_t t, double* s_row, double* qrow)
     for (int64_t j = 0; j < n_vis; j++) {
         const double p = s_row[j];
         for (int64_t c = 0; c < d; c++)
-            o[c] += p * decode_one(jb->v, slice + j * d + c, jb->dtype);
+            o[c] += p * decode_one(jb->v, kv_slice + j * d + c, jb->dtype);
     }
 
     if (jb->lse)
@@ -176,12 +185,14 @@ static void* worker(void* arg)
 }
 
 static int check_args(const void* q, const void* k, const void* v,
-                      int64_t B, int64_t H, int64_t N, int64_t d,
+                      int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
                       int causal, float scale, int dtype)
 {
     if (!q || !k || !v)
         return ATTN_REF_EINVAL;
     if (B <= 0 || H <= 0 || N <= 0 || d <= 0)
+        return ATTN_REF_EINVAL;
+    if (H_kv <= 0 || H % H_kv != 0)
         return ATTN_REF_EINVAL;
     if (causal != 0 && causal != 1)
         return ATTN_REF_EINVAL;
@@ -221,13 +232,13 @@ static int run_job(job_t* jb, int num_threads)
     return jb->failed ? ATTN_REF_ENOMEM : ATTN_REF_OK;
 }
 
-int attn_fwd_ref_rows(const void* q, const void* k, const void* v,
-                      int64_t B, int64_t H, int64_t N, int64_t d,
-                      int causal, float scale, int dtype,
-                      const int64_t* rows, int64_t n_rows,
-                      double* o_rows, double* lse_rows, int num_threads)
+int attn_fwd_ref_rows_gqa(const void* q, const void* k, const void* v,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                          int causal, float scale, int dtype,
+                          const int64_t* rows, int64_t n_rows,
+                          double* o_rows, double* lse_rows, int num_threads)
 {
-    int rc = check_args(q, k, v, B, H, N, d, causal, scale, dtype);
+    int rc = check_args(q, k, v, B, H, H_kv, N, d, causal, scale, dtype);
     if (rc != ATTN_REF_OK)
         return rc;
     if (n_rows < 0 || (n_rows > 0 && (!rows || !o_rows)))
@@ -241,7 +252,7 @@ int attn_fwd_ref_rows(const void* q, const void* k, const void* v,
     job_t jb;
     memset(&jb, 0, sizeof jb);
     jb.q = q; jb.k = k; jb.v = v;
-    jb.B = B; jb.H = H; jb.N = N; jb.d = d;
+    jb.B = B; jb.H = H; jb.H_kv = H_kv; jb.N = N; jb.d = d;
     jb.causal = causal;
     jb.scale = (double)scale;
     jb.dtype = dtype;
@@ -252,12 +263,12 @@ int attn_fwd_ref_rows(const void* q, const void* k, const void* v,
     return run_job(&jb, num_threads);
 }
 
-int attn_fwd_ref(const void* q, const void* k, const void* v,
-                 double* o_ref, double* lse_ref,
-                 int64_t B, int64_t H, int64_t N, int64_t d,
-                 int causal, float scale, int dtype, int num_threads)
+int attn_fwd_ref_gqa(const void* q, const void* k, const void* v,
+                     double* o_ref, double* lse_ref,
+                     int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                     int causal, float scale, int dtype, int num_threads)
 {
-    int rc = check_args(q, k, v, B, H, N, d, causal, scale, dtype);
+    int rc = check_args(q, k, v, B, H, H_kv, N, d, causal, scale, dtype);
     if (rc != ATTN_REF_OK)
         return rc;
     if (!o_ref)
@@ -268,8 +279,27 @@ int attn_fwd_ref(const void* q, const void* k, const void* v,
         return ATTN_REF_ENOMEM;
     for (int64_t r = 0; r < n; r++)
         rows[r] = r;   /* every row, in storage order: o_rows == o_ref */
-    rc = attn_fwd_ref_rows(q, k, v, B, H, N, d, causal, scale, dtype,
-                           rows, n, o_ref, lse_ref, num_threads);
+    rc = attn_fwd_ref_rows_gqa(q, k, v, B, H, H_kv, N, d, causal, scale, dtype,
+                               rows, n, o_ref, lse_ref, num_threads);
     free(rows);
     return rc;
+}
+
+int attn_fwd_ref_rows(const void* q, const void* k, const void* v,
+                      int64_t B, int64_t H, int64_t N, int64_t d,
+                      int causal, float scale, int dtype,
+                      const int64_t* rows, int64_t n_rows,
+                      double* o_rows, double* lse_rows, int num_threads)
+{
+    return attn_fwd_ref_rows_gqa(q, k, v, B, H, H, N, d, causal, scale, dtype,
+                                 rows, n_rows, o_rows, lse_rows, num_threads);
+}
+
+int attn_fwd_ref(const void* q, const void* k, const void* v,
+                 double* o_ref, double* lse_ref,
+                 int64_t B, int64_t H, int64_t N, int64_t d,
+                 int causal, float scale, int dtype, int num_threads)
+{
+    return attn_fwd_ref_gqa(q, k, v, o_ref, lse_ref, B, H, H, N, d, causal, scale,
+                            dtype, num_threads);
 }

@@ -45,7 +45,7 @@ def test_every_header_is_covered():
 
 def test_attn_library_exports_header(attn_lib_path):
     decl = _declared_functions("attn.h")
-    assert decl == ["attn_fwd", "attn_strerror"]
+    assert decl == ["attn_fwd", "attn_fwd_gqa", "attn_strerror"]
     missing = set(decl) - _exported(attn_lib_path)
     assert not missing, missing
     ctypes.CDLL(attn_lib_path)   # loads without a GPU
@@ -53,7 +53,8 @@ def test_attn_library_exports_header(attn_lib_path):
 
 def test_oracle_library_exports_header(oracle_lib):
     decl = _declared_functions("attn_ref.h")
-    assert decl == ["attn_fwd_ref", "attn_fwd_ref_rows", "attn_ref_decode"]
+    assert decl == ["attn_fwd_ref", "attn_fwd_ref_gqa", "attn_fwd_ref_rows",
+                    "attn_fwd_ref_rows_gqa", "attn_ref_decode"]
     missing = set(decl) - _exported(oracle_lib.LIB_PATH)
     assert not missing, missing
 
@@ -111,6 +112,17 @@ def test_argument_validation(attn_lib_path):
         rc = ea.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
                          a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
         assert rc == want, (change, rc)
+        # The grouped-query entry point with H_kv = H validates identically.
+        rc = ea.attn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                             a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"],
+                             a["stream"])
+        assert rc == want, ("gqa", change, rc)
+    # K/V head counts that do not divide H (or are not positive) are refused.
+    for H, H_kv in [(2, 0), (2, -2), (6, 4), (4, 3), (1, 2), (8, 16)]:
+        a = dict(good, H=H)
+        rc = ea.attn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], H, H_kv,
+                             a["N"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+        assert rc == ea.ATTN_EINVAL, (H, H_kv, rc)
 
 
 def test_python_wrapper_checks(attn_lib_path):
@@ -119,6 +131,11 @@ def test_python_wrapper_checks(attn_lib_path):
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         ea.fwd(q, q, q)   # host tensors are refused before any call
+    q4 = torch.zeros(1, 4, 8, 64)
+    with pytest.raises(ValueError):
+        ea.fwd(q4, q4[:, :3], q4[:, :3])   # 3 K/V heads do not divide 4
+    with pytest.raises(ValueError):
+        ea.fwd(q4, q4[:, :2], q4[:, :1])   # k and v differ
     with pytest.raises(TypeError):
         ea.dtype_code(torch.float64)
     assert ea.default_scale(64) == 0.125

@@ -68,6 +68,32 @@ def test_sweep_small(ea, oracle_lib, dtype, d, causal):
         _check(o, lse, o_ref, lse_ref, dtype, f"N={n} d={d} {dtype} causal={causal}")
 
 
+GQA_HEADS = [(4, 1), (4, 2), (6, 3), (8, 2), (16, 4)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16],
+                         ids=["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_gqa_small(ea, oracle_lib, dtype, d, causal):
+    """Grouped-query and multi-query attention, every output element, with
+    B = 2 so that both the head grouping and the batch offset of K/V matter;
+    the GPU result with shared K/V heads is also bit-identical to the
+    multi-head launch on K/V expanded to one head per query head."""
+    for (H, H_kv), n in zip(GQA_HEADS, [1, 65, 130, 200, 257]):
+        q, k, v = make_qkv(2, H, n, d, dtype, seed=8000 + 7 * H + H_kv + n, H_kv=H_kv)
+        scale = ea.default_scale(d)
+        o_ref, lse_ref = oracle_lib.attn_fwd_ref(q, k, v, causal, scale)
+        o, lse = _run_gpu(ea, q, k, v, causal, scale)
+        _check(o, lse, o_ref, lse_ref, dtype,
+               f"GQA H={H} H_kv={H_kv} N={n} d={d} {dtype} causal={causal}")
+        G = H // H_kv
+        ke = k.repeat_interleave(G, dim=1).contiguous()
+        ve = v.repeat_interleave(G, dim=1).contiguous()
+        o2, lse2 = _run_gpu(ea, q, ke, ve, causal, scale)
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
 def _sample_rows(B, H, N, rng, n_random=192):
     BH = B * H
     rows = set()

@@ -386,6 +386,76 @@ def test_online_recurrence_matches_definition(orc, bn, causal):
     np.testing.assert_allclose(lse2, lse, rtol=1e-13, atol=1e-13)
 
 
+# ------------------------------------------------ grouped-query attention
+# ('Flash Attention v2 的核心优化原理与工程实现', References item 5: Flash
+# Attention with GQA; query head h reads K/V head h // (H // H_kv)).
+
+@pytest.mark.parametrize("H,H_kv", [(4, 2), (6, 3), (4, 1), (8, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_library_on_expanded_kv(orc, H, H_kv, causal):
+    """GQA = MHA with each K/V head repeated for its group of query heads
+    (library fp64 softmax on repeat_interleave'd K/V). A grouping by h % H_kv
+    instead of h // G gives different heads and fails here."""
+    g = torch.Generator().manual_seed(31 + H * 10 + H_kv)
+    q = torch.randn(2, H, 13, 8, generator=g).to(torch.bfloat16)
+    k = torch.randn(2, H_kv, 13, 8, generator=g).to(torch.bfloat16)
+    v = torch.randn(2, H_kv, 13, 8, generator=g).to(torch.bfloat16)
+    G = H // H_kv
+    ke, ve = k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1)
+    o, lse = orc.attn_fwd_ref(q, k, v, causal, 0.375)
+    o2, lse2, _ = _library_attention(q, ke, ve, causal, 0.375)
+    np.testing.assert_allclose(o, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-13, atol=1e-13)
+    # and the expanded inputs through the oracle's MHA path give the same bits
+    o3, lse3 = orc.attn_fwd_ref(q, ke.contiguous(), ve.contiguous(), causal, 0.375)
+    np.testing.assert_array_equal(o, o3)
+    np.testing.assert_array_equal(lse, lse3)
+
+
+def test_mqa_heads_share_one_kv(orc):
+    """H_kv = 1: every query head of a batch reads the single K/V head, so a
+    query head equal to another's gives identical rows."""
+    g = torch.Generator().manual_seed(41)
+    q = torch.randn(2, 3, 9, 8, generator=g)
+    q[:, 2] = q[:, 0]
+    k = torch.randn(2, 1, 9, 8, generator=g)
+    v = torch.randn(2, 1, 9, 8, generator=g)
+    o, lse = orc.attn_fwd_ref(q, k, v, True, 0.5)
+    np.testing.assert_array_equal(o[:, 2], o[:, 0])
+    assert not np.array_equal(o[0], o[1])   # batches use their own K/V
+    for b in range(2):
+        for h in range(3):
+            o1, l1 = orc.attn_fwd_ref(q[b:b + 1, h:h + 1], k[b:b + 1], v[b:b + 1], True, 0.5)
+            np.testing.assert_array_equal(o1[0, 0], o[b, h])
+            np.testing.assert_array_equal(l1[0, 0], lse[b, h])
+
+
+def test_gqa_rows_api_matches_full(orc):
+    q, _, _ = make_qkv(2, 4, 30, 16, torch.float16, seed=42)
+    _, k, v = make_qkv(2, 2, 30, 16, torch.float16, seed=43)
+    o, lse = orc.attn_fwd_ref(q, k, v, False, 0.25)
+    rows = np.array([0, 29, 30, 61, 119, 200, 239])
+    o_r, l_r = orc.attn_fwd_ref_rows(q, k, v, False, 0.25, rows)
+    np.testing.assert_array_equal(o_r, o.reshape(-1, 16)[rows])
+    np.testing.assert_array_equal(l_r, lse.reshape(-1)[rows])
+
+
+def test_gqa_rejects_bad_head_counts(orc):
+    import ctypes
+    lib = orc._load()
+    q, k, v = make_qkv(1, 4, 4, 4, torch.float32, seed=1)
+    o = np.zeros((1, 4, 4, 4))
+    dp = o.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    for H_kv, want in [(4, 0), (2, 0), (1, 0), (3, -1), (0, -1), (-2, -1), (8, -1)]:
+        rc = lib.attn_fwd_ref_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), dp, None,
+                                  1, 4, H_kv, 4, 4, 0, 1.0, 0, 1)
+        assert rc == want, (H_kv, rc)
+    with pytest.raises(RuntimeError):
+        orc.attn_fwd_ref(q, k[:, :3], v[:, :3], False, 1.0)   # 3 does not divide 4
+    with pytest.raises(ValueError):
+        orc.attn_fwd_ref(q, k[:, :2], v[:, :1], False, 1.0)   # k, v shapes differ
+
+
 # ------------------------------------------------------------ errors
 
 def test_oracle_rejects_bad_arguments(orc):
