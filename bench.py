@@ -6,6 +6,8 @@ Default workload: bf16, causal, B=4, H=16, N=4096, d=64.
 
 Prints ONE JSON line with the attention TFLOPS, its roofline fraction and
 the CPU fp64 oracle timed on a bounded sample of the same workload.
+``--pass bwd`` times the backward pass (dQ, dK, dV) instead: one step is one
+attn_bwd call (its three kernels) with q, k, v, o, lse and dO resident.
 
 FLOP convention (every page's): 4*B*H*N^2*d per forward, halved for causal —
 checked against the figures printed in "Flash Attention（二）v2版本朴素实现
@@ -71,6 +73,14 @@ def measured_traffic(workload: str):
     return entry["hbm_bytes_per_launch"]
 
 
+def bwd_flops(B, H, N, d, causal) -> float:
+    """Five N x N x d products (dV, dP, dQ, dK and the recomputed S): 2.5x the
+    forward's two, halved for causal — the convention that sets backward
+    FLOPs against the forward's. The dQ kernel's second S and dP products
+    are not counted."""
+    return 2.5 * attention_flops(B, H, N, d, causal)
+
+
 def cpu_baseline(w, q, k, v, n_slices: int):
     import numpy as np
     import oracle
@@ -87,6 +97,126 @@ def cpu_baseline(w, q, k, v, n_slices: int):
                       f"({flops / 1e9:.1f} GFLOP by the same convention), {dt:.2f} s wall"}
 
 
+def cpu_baseline_bwd(w, q, k, v, dout, n_kv: int):
+    """The oracle's backward on the first n_kv K/V slices (each with its query
+    heads), timed on the host cores."""
+    import oracle
+
+    oracle.build() if not os.path.exists(oracle.LIB_PATH) else None
+    threads = len(os.sched_getaffinity(0))
+    G = w.H // w.kv_heads
+    dt = 0.0
+    for s in range(n_kv):
+        b, hk = divmod(s, w.kv_heads)
+        hs = slice(hk * G, (hk + 1) * G)
+        sub = tuple(t.contiguous() for t in (q[b:b + 1, hs], k[b:b + 1, hk:hk + 1],
+                                             v[b:b + 1, hk:hk + 1], dout[b:b + 1, hs]))
+        t0 = time.perf_counter()
+        oracle.attn_bwd_ref(*sub, w.causal, w.scale, num_threads=threads)
+        dt += time.perf_counter() - t0
+    flops = bwd_flops(1, n_kv * G, w.N, w.d, w.causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"backward of {n_kv} of {w.B * w.kv_heads} K/V slices with their "
+                      f"{G} query head(s) each, all {w.N} rows "
+                      f"({flops / 1e9:.1f} GFLOP by the same convention), {dt:.2f} s wall"}
+
+
+def run_bwd(args, name, w):
+    """Backward-pass bench line (``--pass bwd``)."""
+    import numpy as np
+    import torch
+
+    import exact_attention_15_amd as ea
+    from exact_attention_15_amd.inputs import workload_dout, workload_inputs
+
+    dt_name = DTYPE_NAME[str(w.dtype)]
+    if dt_name == "fp32":
+        print("bench.py: the backward pass takes fp16 / bf16 inputs", file=sys.stderr)
+        sys.exit(2)
+    ea.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = workload_inputs(w)
+    dout = workload_dout(w)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, dout))
+    o, lse = ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    G = w.H // w.kv_heads
+    out = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd),
+           torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev))
+
+    parity = None
+    if not args.no_check:
+        # First K/V slice: o / lse from the oracle, gradients against the
+        # oracle's, within the first-order rounding bound of the parity tests.
+        import oracle
+        sub = tuple(t.contiguous() for t in (q[:1, :G], k[:1, :1], v[:1, :1], dout[:1, :G]))
+        o_r, l_r = oracle.attn_fwd_ref(sub[0], sub[1], sub[2], w.causal, w.scale)
+        o[:1, :G] = torch.from_numpy(o_r).to(w.dtype).to(dev)
+        lse[:1, :G] = torch.from_numpy(l_r).to(torch.float32).to(dev)
+        grads = ea.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, out=out)
+        torch.cuda.synchronize()
+        ref = oracle.attn_bwd_ref(*sub, w.causal, w.scale, error_scales=True)
+        u = 2.0 ** -8 if dt_name == "bf16" else 2.0 ** -11
+        s_half = 2.0 ** -134 if dt_name == "bf16" else 2.0 ** -25
+        worst = 0.0
+        for got, r, e, z in zip((grads[0][:1, :G], grads[1][:1, :1], grads[2][:1, :1]),
+                                ref[:3], ref[3:6], ref[6:9]):
+            diff = np.abs(got.cpu().double().numpy() - r)
+            bound = 2 * ((u + (G * w.N / 16 + 32) * 2.0 ** -24) * (e + np.abs(r)) +
+                         s_half * (z + 1))
+            worst = max(worst, float((diff / bound).max()))
+        parity = worst
+        if not worst <= 1.0:
+            print(f"bench.py: backward parity gate failed: err/bound {worst:.3f}", file=sys.stderr)
+            sys.exit(1)
+
+    for _ in range(args.warmup):
+        ea.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        ea.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, out=out)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(stop) / args.steps
+    flops = bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dt_name]
+    line = {
+        "metric": "attention bwd TFLOPS (dQ, dK, dV; 2.5x forward FLOPs); % of MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name,
+        "data": "synthetic (seeded i.i.d. N(0,1) inputs and dO rounded to the dtype)",
+        "config": {"workload": w.describe().replace("fwd", "bwd"), "name": name, "B": w.B,
+                   "H": w.H, "H_kv": w.kv_heads, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": w.scale},
+        "pct_of_peak": round(100 * tflops / peak, 2),
+        # One attn_bwd call (three kernels) is the unit timed here.
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+        "parity_err_over_bound_slice0": parity,
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        n_kv = max(1, min(args.cpu_slices or 4, w.B * w.kv_heads))
+        line["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, dout, n_kv)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,8 +225,11 @@ def main():
     # its sustained clocks; fewer warm-up launches time a ramping clock.
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--cpu-slices", type=int, default=64,
-                    help="(b,h) slices the CPU oracle baseline runs on (capped at B*H)")
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd",
+                    help="time the forward (default) or the backward pass")
+    ap.add_argument("--cpu-slices", type=int, default=None,
+                    help="slices the CPU oracle baseline runs on: (b,h) slices for the forward "
+                         "(default 64), K/V slices for the backward (default 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity gate")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -127,6 +260,9 @@ def main():
 
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
+    if args.pass_ == "bwd":
+        run_bwd(args, name, w)
+        return
     dt_name = DTYPE_NAME[str(w.dtype)]
     ea.load_library()
     dev = torch.device("cuda:0")
@@ -203,7 +339,7 @@ def main():
         "wall_s_timed_region": round(t_wall, 4),
     }
     if not args.no_cpu_baseline:
-        n_sl = max(1, min(args.cpu_slices, w.B * w.H))
+        n_sl = max(1, min(args.cpu_slices or 64, w.B * w.H))
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, n_sl)
     print(json.dumps(line), flush=True)
 

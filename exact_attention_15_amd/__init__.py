@@ -44,6 +44,9 @@ def load_library():
     lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.attn_fwd_gqa.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                             ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_bwd.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -128,5 +131,67 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None):
     return o, lse
 
 
-__all__ = ["fwd", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, causal, scale,
+             dtype, stream) -> int:
+    """Raw C-ABI call of the backward pass with integer pointers."""
+    return load_library().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d,
+                                   int(causal), float(scale), int(dtype), stream)
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, out=None):
+    """dq, dk, dv = gradients of the forward pass for the incoming gradient
+    ``dout`` of ``o``, from the forward's ``o`` and ``lse``.
+
+    q, o, dout: [B,H,N,d]; k, v: [B,H_kv,N,d]; lse: float32 [B,H,N]; all on
+    one GPU, contiguous, q/k/v/o/dout of one 16-bit dtype. ``out`` may pass
+    preallocated ``(dq, dk, dv, delta)`` (delta: float32 [B,H,N], written
+    with the row statistic D_i = dout_i . o_i).
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or \
+            (k.shape[0], k.shape[2], k.shape[3]) != (q.shape[0], q.shape[2], q.shape[3]):
+        raise ValueError("need q [B, H, N, d] and k, v [B, H_kv, N, d]")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must match q")
+    if k.shape[1] < 1 or q.shape[1] % k.shape[1] != 0:
+        raise ValueError(f"K/V heads ({k.shape[1]}) must divide query heads ({q.shape[1]})")
+    if len({t.dtype for t in (q, k, v, o, dout)}) != 1:
+        raise TypeError("q, k, v, o, dout must share one dtype")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, N]")
+    for t in (q, k, v, o, lse, dout):
+        if t.device.type != "cuda" or t.device != q.device:
+            raise ValueError("all tensors must be on one GPU device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv, delta = out
+        for t, ref in ((dq, q), (dk, k), (dv, v)):
+            if t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous() \
+                    or t.device != q.device:
+                raise ValueError("out gradients must match q, k, v")
+        if delta.shape != (B, H, N) or delta.dtype != torch.float32 or \
+                not delta.is_contiguous() or delta.device != q.device:
+            raise ValueError("out[3] must be float32 [B, H, N] on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      delta.data_ptr(), B, H, H_kv, N, d, causal, scale,
+                      dtype_code(q.dtype), stream)
+    if rc != ATTN_OK:
+        raise AttnError(rc, strerror(rc))
+    return dq, dk, dv
+
+
+__all__ = ["fwd", "bwd", "attn_bwd", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
            "dtype_code", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -65,6 +65,44 @@ extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                        int causal, float scale, int dtype, void* stream) {
+    int rc = validate(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (!dout || !dq || !dk || !dv || !delta) return ATTN_EINVAL;
+    // The row-statistic kernel covers 16 rows or more per workgroup.
+    if (B * H * N / 16 >= (int64_t)INT32_MAX) return ATTN_EINVAL;
+    if (dtype == ATTN_F32) return ATTN_EUNSUPPORTED;
+    const uintptr_t mis = ((uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u;
+    if (mis != 0 || ((uintptr_t)delta & 3u) != 0) return ATTN_EALIGN;
+
+    attn::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.delta = delta;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.N = N;
+    p.BH = (int)(B * H);
+    p.BH_kv = (int)(B * H_kv);
+    p.H_kv = (int)H_kv;
+    p.G = (int)(H / H_kv);
+    p.scale = scale;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+
+    (void)hipGetLastError();
+    const hipError_t e = attn::launch_bwd16(p, dtype == ATTN_BF16, (int)d, causal != 0,
+                                            (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                         int dtype, void* stream) {
@@ -75,7 +113,7 @@ extern "C" const char* attn_strerror(int code) {
     switch (code) {
         case ATTN_OK: return "ok";
         case ATTN_EINVAL: return "invalid argument (pointer, size, H_kv, dtype, scale or causal)";
-        case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128)";
+        case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128), or fp32 in attn_bwd";
         case ATTN_EALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
         case ATTN_EHIP: return "HIP kernel launch failed";
         default: return "unknown error code";

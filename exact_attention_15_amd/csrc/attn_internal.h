@@ -41,11 +41,33 @@ __device__ __forceinline__ SliceIds slice_of(const FwdParams& p, int r) {
     return {b * p.H_kv * p.G + h, kv_bh};
 }
 
+// Backward pass (gradients of the forward above).
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    float* delta;       // D_i = dO_i . O_i, written by the first kernel
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t N;
+    int BH;             // B * H query slices
+    int BH_kv;          // B * H_kv key/value slices
+    int H_kv;
+    int G;              // H / H_kv
+    float scale;        // multiplied into dQ and dK
+    float scale_log2;   // scale * log2(e)
+};
+
 // Query rows per workgroup for every kernel here.
 constexpr int kBlockM = 128;
 
 // Launchers return the hipError_t of the launch.
 hipError_t launch_fwd16(const FwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd32(const FwdParams& p, int d, bool causal, hipStream_t s);
+hipError_t launch_bwd16(const BwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s);
 
 }  // namespace attn

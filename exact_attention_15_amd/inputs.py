@@ -96,5 +96,17 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
     return tuple(out)
 
 
+def make_dout(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int):
+    """The incoming gradient of O for the backward pass: i.i.d. N(0,1) fp32
+    from its own generator (seed + 10**6), rounded to the dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 10 ** 6)
+    return torch.randn((B, H, N, d), dtype=torch.float32, generator=g).to(dtype).contiguous()
+
+
+def workload_dout(w: Workload):
+    return make_dout(w.B, w.H, w.N, w.d, w.dtype, w.seed)
+
+
 def workload_inputs(w: Workload):
     return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.value_scale, w.H_kv)

@@ -38,7 +38,7 @@ typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
 enum {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,       /* bad argument (null pointer, size, H_kv, dtype, scale, causal) */
-    ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128 */
+    ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128; fp32 in attn_bwd */
     ATTN_EALIGN = -3,       /* a base pointer not 16-byte aligned */
     ATTN_EHIP = -4          /* the HIP launch failed */
 };
@@ -94,6 +94,48 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                  int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int causal,
                  float scale, int dtype, void* stream);
+
+/*
+ * attn_bwd — gradients of the forward pass (of attn_fwd_gqa; H_kv = H for
+ * attn_fwd) for an incoming gradient dout of o. The pages name the backward
+ * pass that consumes the saved row statistics ([FA2-principles], comparison
+ * section); its formulas are the chain rule of the forward definition:
+ *   p_ij  = exp(s_ij - lse_i),  s_ij = scale * q[b,h,i,:] . k[b,h/G,j,:]
+ *   D_i   = sum_c dout[b,h,i,c] * o[b,h,i,c]
+ *   ds_ij = p_ij * (dout[b,h,i,:] . v[b,h/G,j,:] - D_i)
+ *   dq[b,h,i,:]   = scale * sum_j ds_ij k[b,h/G,j,:]
+ *   dk[b,h_kv,j,:] = scale * sum over h with h/G = h_kv, and i, of ds_ij q[b,h,i,:]
+ *   dv[b,h_kv,j,:] = sum over the same h, i of p_ij dout[b,h,i,:]
+ * with j over the visible keys of row i (all, or j <= i when causal = 1).
+ *
+ * q, o, dout   DEVICE pointers, [B,H,N,d] contiguous, `dtype`, 16-byte aligned:
+ *              the forward inputs, its output o and the incoming gradient.
+ * k, v         DEVICE pointers, [B,H_kv,N,d] contiguous, `dtype`, 16-byte aligned.
+ * lse          DEVICE pointer, [B,H,N] fp32: the forward's log-sum-exp.
+ * dq           DEVICE pointer, [B,H,N,d] `dtype`, 16-byte aligned; written.
+ * dk, dv       DEVICE pointers, [B,H_kv,N,d] `dtype`, 16-byte aligned; written
+ *              (not accumulated into).
+ * delta        DEVICE pointer, [B,H,N] fp32, 4-byte aligned; written with D_i
+ *              (fp32 dot product of the stored o and dout rows). It holds the
+ *              row statistic the gradient kernels share, so that the call
+ *              allocates nothing; its contents are valid after the call.
+ * B, H, H_kv, N, d, causal, scale
+ *              as for attn_fwd_gqa.
+ * dtype        ATTN_F16 or ATTN_BF16 (fp32: ATTN_EUNSUPPORTED). Products are
+ *              accumulated in fp32; p and ds are rounded to `dtype` as the
+ *              operands of the dv, dk and dq products; outputs are rounded
+ *              once (nearest even) from fp32.
+ * stream       hipStream_t (NULL = the null stream).
+ *
+ * Asynchronous: three kernels are enqueued on `stream` and the call returns;
+ * no host synchronisation, no device allocation, no atomics (results do not
+ * depend on scheduling). Validation precedes any HIP call. Outputs must not
+ * alias inputs or each other.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, float* delta,
+             int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int causal,
+             float scale, int dtype, void* stream);
 
 /* attn_strerror — static description of a return code (never NULL). */
 const char* attn_strerror(int code);

@@ -97,6 +97,40 @@ int attn_fwd_ref_rows_gqa(const void* q, const void* k, const void* v,
                           const int64_t* rows, int64_t n_rows,
                           double* o_rows, double* lse_rows, int num_threads);
 
+/*
+ * attn_bwd_ref — gradients of the forward definition above for an incoming
+ * dO, in fp64, by the chain rule (the pages name the backward pass without
+ * stating it: "Flash Attention v2 的核心优化原理与工程实现", comparison
+ * section; the forward definition is [naive-attn] section 1.1.2):
+ *   p_ij = softmax_j(scale q_i . k_j over the visible keys), o_i = sum_j p_ij v_j,
+ *   D_i = dO_i . o_i, ds_ij = p_ij (dO_i . v_j - D_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ *   dv_j = sum_i p_ij dO_i,
+ * the sums over i running over every query head that reads K/V head j's head
+ * (grouped-query attention as in attn_fwd_ref_gqa).
+ *
+ * q, dout      host, [B,H,N,d] in `dtype`; k, v host, [B,H_kv,N,d].
+ * dq           host double [B,H,N,d]; dk, dv host double [B,H_kv,N,d].
+ * eq, ek, ev, zq, zk, zv
+ *              optional (all NULL or all non-NULL), shaped like dq, dk, dv,
+ *              dq, dk, dv: error scales. With A_i = sum_c |dO_ic o_ic|,
+ *              w_ij = |ds_ij| + p_ij A_i, g_i = sum_c |dO_ic|, z_ij = 1 + p_ij g_i:
+ *              eq_ic = scale sum_j w_ij |k_jc|, ek_jc = scale sum_i w_ij |q_ic|,
+ *              ev_jc = sum_i p_ij |dO_ic|, zq_ic = scale sum_j z_ij |k_jc|,
+ *              zk_jc = scale sum_i z_ij |q_ic|, zv_jc = sum_i |dO_ic|. To first
+ *              order, rounding p, ds and o to a type whose rounding error is
+ *              at most u |x| + s/2 (s: its subnormal spacing) moves each
+ *              gradient element by at most u e + (s/2) z.
+ * Other arguments and return codes as for attn_fwd_ref_gqa. Synchronous;
+ * parallel over query rows within each K/V slice.
+ */
+int attn_bwd_ref(const void* q, const void* k, const void* v, const void* dout,
+                 double* dq, double* dk, double* dv,
+                 double* eq, double* ek, double* ev,
+                 double* zq, double* zk, double* zv,
+                 int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                 int causal, float scale, int dtype, int num_threads);
+
 /* attn_ref_decode — widen n elements of `dtype` to double, exactly, from the
  * format definitions (sign, exponent, mantissa). Exposed so the decoder can
  * be checked against every 16-bit pattern. Returns ATTN_REF_OK or EINVAL. */

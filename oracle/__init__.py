@@ -66,6 +66,10 @@ def _load():
                                           ctypes.POINTER(ctypes.c_int64), i64, dp, dp,
                                           ctypes.c_int]
     lib.attn_fwd_ref_rows_gqa.restype = ctypes.c_int
+    lib.attn_bwd_ref.argtypes = [vp, vp, vp, vp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                 i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                 ctypes.c_int, ctypes.c_int]
+    lib.attn_bwd_ref.restype = ctypes.c_int
     lib.attn_ref_decode.argtypes = [vp, dp, i64, ctypes.c_int]
     lib.attn_ref_decode.restype = ctypes.c_int
     _lib = lib
@@ -139,6 +143,34 @@ def attn_fwd_ref_rows(q, k, v, causal: bool, scale: float, rows, num_threads: in
     if rc != 0:
         raise RuntimeError(f"attn_fwd_ref_rows failed with code {rc}")
     return o, lse
+
+
+def attn_bwd_ref(q, k, v, dout, causal: bool, scale: float, error_scales: bool = False,
+                 num_threads: int = 0):
+    """Gradients (dq, dk, dv) of the forward definition for the incoming
+    gradient dout, by the chain rule in fp64. q, dout: CPU [B,H,N,d];
+    k, v: CPU [B,H_kv,N,d]; one dtype.
+
+    With ``error_scales`` also returns (eq, ek, ev, zq, zk, zv): rounding p,
+    ds and o to a type with rounding error u|x| + s/2 moves each gradient
+    element by at most u e + (s/2) z to first order (see include/attn_ref.h).
+    """
+    lib = _load()
+    q, k, v, dout = _as_host(q), _as_host(k), _as_host(v), _as_host(dout)
+    B, H, N, d = q.shape
+    H_kv = _kv_heads(q, k, v)
+    if tuple(dout.shape) != tuple(q.shape) or dout.dtype != q.dtype:
+        raise ValueError("oracle: dout must match q")
+    outs = [np.empty((B, H, N, d)), np.empty((B, H_kv, N, d)), np.empty((B, H_kv, N, d))]
+    errs = [np.empty_like(a) for a in outs + outs] if error_scales else [None] * 6
+    ptr = lambda a: None if a is None else _dptr(a)   # noqa: E731
+    rc = lib.attn_bwd_ref(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                          *(ptr(a) for a in outs), *(ptr(a) for a in errs),
+                          B, H, H_kv, N, d, int(bool(causal)), float(scale),
+                          _dtype_code(q), int(num_threads))
+    if rc != 0:
+        raise RuntimeError(f"attn_bwd_ref failed with code {rc}")
+    return tuple(outs) + (tuple(errs) if error_scales else ())
 
 
 def decode(t) -> np.ndarray:

@@ -303,3 +303,258 @@ int attn_fwd_ref(const void* q, const void* k, const void* v,
     return attn_fwd_ref_gqa(q, k, v, o_ref, lse_ref, B, H, H, N, d, causal, scale,
                             dtype, num_threads);
 }
+
+/* ---- backward: the chain rule of the definition above -------------------
+ *
+ * For one query row i (of query head h, K/V head h / (H/H_kv)), with the
+ * visible keys J_i and the softmax row p_ij of the forward definition:
+ *   o_i    = sum_j p_ij v_j
+ *   D_i    = sum_c dO_ic o_ic
+ *   dp_ij  = dO_i . v_j
+ *   ds_ij  = p_ij (dp_ij - D_i)          (derivative through the softmax)
+ *   dq_i   = scale sum_j ds_ij k_j        (s_ij = scale q_i . k_j)
+ *   dk_j  += scale ds_ij q_i
+ *   dv_j  += p_ij dO_i                    (o_i = sum_j p_ij v_j)
+ * Every query row of every query head that shares a K/V head adds into that
+ * head's dk and dv.
+ *
+ * Optional error scales: first-order magnitudes of the terms that a
+ * computation rounding p, ds and o to a floating-point type perturbs. With
+ * A_i = sum_c |dO_ic o_ic| and w_ij = |ds_ij| + p_ij A_i (relative rounding),
+ *   eq_ic = scale sum_j w_ij |k_jc|,  ek_jc = scale sum_i w_ij |q_ic|,
+ *   ev_jc = sum_i p_ij |dO_ic|;
+ * with g_i = sum_c |dO_ic| and z_ij = 1 + p_ij g_i (absolute rounding, a
+ * type's subnormal spacing),
+ *   zq_ic = scale sum_j z_ij |k_jc|,  zk_jc = scale sum_i z_ij |q_ic|,
+ *   zv_jc = sum_i |dO_ic|.
+ */
+
+typedef struct {
+    const void *q, *dout;
+    const double *kd, *vd;      /* this K/V slice, decoded, [N, d] */
+    const double *ka;           /* |kd| */
+    int64_t N, d;
+    int causal;
+    double scale;
+    int dtype;
+    int64_t q_head0;            /* b*H + h of the slice's first query head */
+    int64_t row_begin, row_end; /* t in [0, G*N): head q_head0 + t/N, row t%N */
+    double *dq, *eq;            /* [B,H,N,d] outputs (eq may be NULL) */
+    double *zq;                 /* may be NULL */
+    double *dk, *dv, *ek, *ev;  /* this worker's partial sums, [N, d] */
+    double *zk, *zv;
+    double *work;               /* 3N + 5d doubles */
+} bwd_part_t;
+
+static void bwd_row(bwd_part_t* w, int64_t t)
+{
+    const int64_t N = w->N, d = w->d;
+    const int64_t hh = t / N, i = t % N;
+    const int64_t row_off = ((w->q_head0 + hh) * N + i) * d;
+    const int64_t n_vis = w->causal ? i + 1 : N;
+    const double* kd = w->kd;
+    const double* vd = w->vd;
+    double* p = w->work;              /* [N] */
+    double* ds = p + N;               /* [N] */
+    double* wt = ds + N;              /* [N] */
+    double* qrow = wt + N;            /* [d] */
+    double* grow = qrow + d;          /* [d]: dO_i */
+    double* orow = grow + d;          /* [d] */
+    double* qa = orow + d;            /* [d]: |q_i| */
+    double* ga = qa + d;              /* [d]: |dO_i| */
+
+    for (int64_t c = 0; c < d; c++) {
+        qrow[c] = decode_one(w->q, row_off + c, w->dtype);
+        grow[c] = decode_one(w->dout, row_off + c, w->dtype);
+        qa[c] = fabs(qrow[c]);
+        ga[c] = fabs(grow[c]);
+    }
+    /* forward row: s_ij, safe softmax p_ij, o_i */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n_vis; j++) {
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; c++)
+            dot += qrow[c] * kd[j * d + c];
+        p[j] = w->scale * dot;
+        if (p[j] > m)
+            m = p[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < n_vis; j++) {
+        p[j] = exp(p[j] - m);
+        l += p[j];
+    }
+    for (int64_t j = 0; j < n_vis; j++)
+        p[j] /= l;
+    for (int64_t c = 0; c < d; c++)
+        orow[c] = 0.0;
+    for (int64_t j = 0; j < n_vis; j++)
+        for (int64_t c = 0; c < d; c++)
+            orow[c] += p[j] * vd[j * d + c];
+
+    double D = 0.0, A = 0.0, gs = 0.0;
+    for (int64_t c = 0; c < d; c++) {
+        D += grow[c] * orow[c];
+        A += fabs(grow[c] * orow[c]);
+        gs += ga[c];
+    }
+    for (int64_t j = 0; j < n_vis; j++) {
+        double dp = 0.0;
+        for (int64_t c = 0; c < d; c++)
+            dp += grow[c] * vd[j * d + c];
+        ds[j] = p[j] * (dp - D);
+        wt[j] = fabs(ds[j]) + p[j] * A;
+    }
+
+    double* dq = w->dq + row_off;
+    for (int64_t c = 0; c < d; c++)
+        dq[c] = 0.0;
+    for (int64_t j = 0; j < n_vis; j++)
+        for (int64_t c = 0; c < d; c++)
+            dq[c] += ds[j] * kd[j * d + c];
+    for (int64_t c = 0; c < d; c++)
+        dq[c] *= w->scale;
+    if (w->eq) {
+        double* eq = w->eq + row_off;
+        for (int64_t c = 0; c < d; c++)
+            eq[c] = 0.0;
+        for (int64_t j = 0; j < n_vis; j++)
+            for (int64_t c = 0; c < d; c++)
+                eq[c] += wt[j] * w->ka[j * d + c];
+        for (int64_t c = 0; c < d; c++)
+            eq[c] *= w->scale;
+        double* zq = w->zq + row_off;
+        for (int64_t c = 0; c < d; c++)
+            zq[c] = 0.0;
+        for (int64_t j = 0; j < n_vis; j++) {
+            const double z = 1.0 + p[j] * gs;
+            for (int64_t c = 0; c < d; c++)
+                zq[c] += z * w->ka[j * d + c];
+        }
+        for (int64_t c = 0; c < d; c++)
+            zq[c] *= w->scale;
+    }
+    for (int64_t j = 0; j < n_vis; j++) {
+        const double a = w->scale * ds[j], pj = p[j];
+        double* dk = w->dk + j * d;
+        double* dv = w->dv + j * d;
+        for (int64_t c = 0; c < d; c++) {
+            dk[c] += a * qrow[c];
+            dv[c] += pj * grow[c];
+        }
+        if (w->ek) {
+            const double b = w->scale * wt[j];
+            const double z = w->scale * (1.0 + pj * gs);
+            double* ek = w->ek + j * d;
+            double* ev = w->ev + j * d;
+            double* zk = w->zk + j * d;
+            double* zv = w->zv + j * d;
+            for (int64_t c = 0; c < d; c++) {
+                ek[c] += b * qa[c];
+                ev[c] += pj * ga[c];
+                zk[c] += z * qa[c];
+                zv[c] += ga[c];
+            }
+        }
+    }
+}
+
+static void* bwd_worker(void* arg)
+{
+    bwd_part_t* w = (bwd_part_t*)arg;
+    for (int64_t t = w->row_begin; t < w->row_end; t++)
+        bwd_row(w, t);
+    return NULL;
+}
+
+int attn_bwd_ref(const void* q, const void* k, const void* v, const void* dout,
+                 double* dq, double* dk, double* dv,
+                 double* eq, double* ek, double* ev,
+                 double* zq, double* zk, double* zv,
+                 int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                 int causal, float scale, int dtype, int num_threads)
+{
+    int rc = check_args(q, k, v, B, H, H_kv, N, d, causal, scale, dtype);
+    if (rc != ATTN_REF_OK)
+        return rc;
+    if (!dout || !dq || !dk || !dv)
+        return ATTN_REF_EINVAL;
+    const int with_e = eq != NULL;
+    if ((ek != NULL) != with_e || (ev != NULL) != with_e || (zq != NULL) != with_e ||
+        (zk != NULL) != with_e || (zv != NULL) != with_e)
+        return ATTN_REF_EINVAL;
+
+    const int64_t G = H / H_kv, rows = G * N, nd = N * d;
+    if (num_threads <= 0) {
+        long n = sysconf(_SC_NPROCESSORS_ONLN);
+        num_threads = n > 0 ? (int)n : 1;
+    }
+    if (num_threads > rows)
+        num_threads = (int)rows;
+    const int T = num_threads;
+    const int n_acc = with_e ? 6 : 2;   /* dk, dv (, ek, ev, zk, zv) per worker */
+
+    double* kd = (double*)malloc((size_t)nd * 3 * sizeof(double));
+    double* part = (double*)calloc((size_t)T * n_acc * nd, sizeof(double));
+    double* work = (double*)malloc((size_t)T * (3 * N + 5 * d) * sizeof(double));
+    bwd_part_t* parts = (bwd_part_t*)calloc((size_t)T, sizeof(bwd_part_t));
+    pthread_t* th = (pthread_t*)malloc((size_t)T * sizeof(pthread_t));
+    if (!kd || !part || !work || !parts || !th) {
+        free(kd); free(part); free(work); free(parts); free(th);
+        return ATTN_REF_ENOMEM;
+    }
+    double* vd = kd + nd;
+    double* ka = vd + nd;
+
+    for (int64_t b = 0; b < B; b++)
+        for (int64_t hkv = 0; hkv < H_kv; hkv++) {
+            const int64_t kv_off = (b * H_kv + hkv) * nd;
+            for (int64_t x = 0; x < nd; x++) {
+                kd[x] = decode_one(k, kv_off + x, dtype);
+                vd[x] = decode_one(v, kv_off + x, dtype);
+                ka[x] = fabs(kd[x]);
+            }
+            memset(part, 0, (size_t)T * n_acc * nd * sizeof(double));
+            int started = 0;
+            for (int t = 0; t < T; t++) {
+                bwd_part_t* w = &parts[t];
+                w->q = q; w->dout = dout; w->kd = kd; w->vd = vd; w->ka = ka;
+                w->N = N; w->d = d; w->causal = causal;
+                w->scale = (double)scale; w->dtype = dtype;
+                w->q_head0 = b * H + hkv * G;
+                w->row_begin = rows * t / T;
+                w->row_end = rows * (t + 1) / T;
+                w->dq = dq; w->eq = eq; w->zq = zq;
+                double* base = part + (size_t)t * n_acc * nd;
+                w->dk = base; w->dv = base + nd;
+                w->ek = with_e ? base + 2 * nd : NULL;
+                w->ev = with_e ? base + 3 * nd : NULL;
+                w->zk = with_e ? base + 4 * nd : NULL;
+                w->zv = with_e ? base + 5 * nd : NULL;
+                w->work = work + (size_t)t * (3 * N + 5 * d);
+            }
+            for (int t = 0; t < T; t++) {
+                if (pthread_create(&th[t], NULL, bwd_worker, &parts[t]) != 0)
+                    break;
+                started++;
+            }
+            for (int t = started; t < T; t++)
+                bwd_worker(&parts[t]);   /* workers that could not start run here */
+            for (int t = 0; t < started; t++)
+                pthread_join(th[t], NULL);
+            /* sum the workers' partial dk, dv (, ek, ev, zk, zv) in worker order */
+            for (int a = 0; a < n_acc; a++) {
+                double* const outs[6] = {dk, dv, ek, ev, zk, zv};
+                double* out = outs[a];
+                out += kv_off;
+                for (int64_t x = 0; x < nd; x++) {
+                    double acc = 0.0;
+                    for (int t = 0; t < T; t++)
+                        acc += part[((size_t)t * n_acc + a) * nd + x];
+                    out[x] = acc;
+                }
+            }
+        }
+    free(kd); free(part); free(work); free(parts); free(th);
+    return ATTN_REF_OK;
+}

@@ -45,7 +45,7 @@ def test_every_header_is_covered():
 
 def test_attn_library_exports_header(attn_lib_path):
     decl = _declared_functions("attn.h")
-    assert decl == ["attn_fwd", "attn_fwd_gqa", "attn_strerror"]
+    assert decl == ["attn_bwd", "attn_fwd", "attn_fwd_gqa", "attn_strerror"]
     missing = set(decl) - _exported(attn_lib_path)
     assert not missing, missing
     ctypes.CDLL(attn_lib_path)   # loads without a GPU
@@ -53,7 +53,7 @@ def test_attn_library_exports_header(attn_lib_path):
 
 def test_oracle_library_exports_header(oracle_lib):
     decl = _declared_functions("attn_ref.h")
-    assert decl == ["attn_fwd_ref", "attn_fwd_ref_gqa", "attn_fwd_ref_rows",
+    assert decl == ["attn_bwd_ref", "attn_fwd_ref", "attn_fwd_ref_gqa", "attn_fwd_ref_rows",
                     "attn_fwd_ref_rows_gqa", "attn_ref_decode"]
     missing = set(decl) - _exported(oracle_lib.LIB_PATH)
     assert not missing, missing
@@ -123,6 +123,46 @@ def test_argument_validation(attn_lib_path):
         rc = ea.attn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], H, H_kv,
                              a["N"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
         assert rc == ea.ATTN_EINVAL, (H, H_kv, rc)
+
+
+def test_bwd_argument_validation(attn_lib_path):
+    """attn_bwd: the forward's checks plus its own pointers, dtype and
+    alignment, all before any HIP call."""
+    import exact_attention_15_amd as ea
+    P = 0x7f0000000000
+    good = dict(q=P, k=P + 0x1000, v=P + 0x2000, o=P + 0x3000, lse=P + 0x4000, dout=P + 0x5000,
+                dq=P + 0x6000, dk=P + 0x7000, dv=P + 0x8000, delta=P + 0x9000,
+                B=1, H=4, H_kv=2, N=128, d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16,
+                stream=None)
+    cases = [
+        (dict(q=None), ea.ATTN_EINVAL),
+        (dict(o=None), ea.ATTN_EINVAL),
+        (dict(lse=None), ea.ATTN_EINVAL),
+        (dict(dout=None), ea.ATTN_EINVAL),
+        (dict(dq=None), ea.ATTN_EINVAL),
+        (dict(dk=None), ea.ATTN_EINVAL),
+        (dict(dv=None), ea.ATTN_EINVAL),
+        (dict(delta=None), ea.ATTN_EINVAL),
+        (dict(H_kv=3), ea.ATTN_EINVAL),
+        (dict(H_kv=0), ea.ATTN_EINVAL),
+        (dict(N=0), ea.ATTN_EINVAL),
+        (dict(causal=-1), ea.ATTN_EINVAL),
+        (dict(scale=float("nan")), ea.ATTN_EINVAL),
+        (dict(dtype=5), ea.ATTN_EINVAL),
+        (dict(d=96), ea.ATTN_EUNSUPPORTED),
+        (dict(dtype=ea.ATTN_F32), ea.ATTN_EUNSUPPORTED),
+        (dict(dout=P + 0x5008), ea.ATTN_EALIGN),
+        (dict(dq=P + 0x6004), ea.ATTN_EALIGN),
+        (dict(dk=P + 0x7002), ea.ATTN_EALIGN),
+        (dict(dv=P + 0x8008), ea.ATTN_EALIGN),
+        (dict(delta=P + 0x9002), ea.ATTN_EALIGN),
+    ]
+    names = ["q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta", "B", "H", "H_kv",
+             "N", "d", "causal", "scale", "dtype", "stream"]
+    for change, want in cases:
+        a = dict(good, **change)
+        rc = ea.attn_bwd(*(a[n] for n in names))
+        assert rc == want, (change, rc)
 
 
 def test_python_wrapper_checks(attn_lib_path):

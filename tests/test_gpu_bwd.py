@@ -1,0 +1,176 @@
+"""GPU parity of the backward pass (dQ, dK, dV) against the CPU fp64 oracle,
+through the C ABI.
+
+Inputs o and lse are the oracle's exact forward values rounded to their
+storage types (o to the input dtype, lse to fp32), so the comparison
+isolates the backward kernels' arithmetic. The bound per gradient element,
+from the error analysis of that arithmetic (first order):
+    |g - g_ref| <= 2 [(u + n_acc 2^-24) (e + |g_ref|) + (s/2) (z + 1)]
+Rounding x to the 16-bit type errs by at most u|x| + s/2: u its unit
+roundoff (2^-8 bf16, 2^-11 fp16), s its subnormal spacing (2^-24 fp16,
+2^-133 bf16). p and ds are rounded to it as matrix-core operands, o was
+rounded to it, and the output is rounded to it; e and z are the oracle's
+error scales of the element (the sums of the magnitudes those roundings
+perturb, relatively and absolutely); n_acc = G N / 16 + 32 bounds the fp32
+accumulator updates behind one element; the factor 2 covers second-order
+terms. Small shapes compare every element; full-size workloads
+compare every element of sampled K/V slices (the oracle recomputes those
+slices alone: slices are independent) and check identities on all others.
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_15_amd.inputs import WORKLOADS, make_dout, make_qkv, workload_dout, \
+    workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+U = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
+SUB = {torch.float16: 2.0 ** -24, torch.bfloat16: 2.0 ** -133}
+
+
+@pytest.fixture(scope="module")
+def ea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_15_amd as ea
+    ea.load_library()
+    return ea
+
+
+def _fwd_stats(oracle_lib, q, k, v, causal, scale):
+    o_ref, lse_ref = oracle_lib.attn_fwd_ref(q, k, v, causal, scale)
+    return torch.from_numpy(o_ref).to(q.dtype), torch.from_numpy(lse_ref).to(torch.float32)
+
+
+def _check(got, ref, err, zerr, dtype, n_acc, what):
+    got = got.to(torch.float64).cpu().numpy() if isinstance(got, torch.Tensor) else got
+    assert np.all(np.isfinite(got)), what
+    bound = 2 * ((U[dtype] + n_acc * 2.0 ** -24) * (err + np.abs(ref)) +
+                 SUB[dtype] / 2 * (zerr + 1))
+    diff = np.abs(got - ref)
+    ratio = float((diff / np.maximum(bound, 1e-300)).max())
+    print(f"{what}: max-abs {float(diff.max()):.3e}, max err/bound {ratio:.3f}", flush=True)
+    assert np.all(diff <= bound), (what, ratio)
+
+
+def _bwd_and_check(ea, oracle_lib, q, k, v, dout, causal, scale, what):
+    o, lse = _fwd_stats(oracle_lib, q, k, v, causal, scale)
+    dq, dk, dv = ea.bwd(*(t.cuda() for t in (q, k, v, o, lse, dout)), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv, eq, ek, ev, zq, zk, zv = oracle_lib.attn_bwd_ref(q, k, v, dout, causal, scale,
+                                                                 error_scales=True)
+    n_acc = (q.shape[1] // k.shape[1]) * q.shape[2] / 16 + 32
+    _check(dq, rq, eq, zq, q.dtype, n_acc, what + " dq")
+    _check(dk, rk, ek, zk, q.dtype, n_acc, what + " dk")
+    _check(dv, rv, ev, zv, q.dtype, n_acc, what + " dv")
+
+
+SWEEP = [(1, 2, 2), (2, 4, 1), (17, 2, 2), (64, 4, 2), (65, 2, 2), (127, 6, 3), (128, 2, 2),
+         (129, 4, 4), (200, 4, 1), (257, 2, 2)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bwd_sweep_small(ea, oracle_lib, dtype, d, causal):
+    """Every gradient element; N across tile edges and ragged tails, with
+    multi-head, grouped-query and multi-query head counts."""
+    for n, H, H_kv in SWEEP:
+        seed = 9000 + 3 * n + H + H_kv + d
+        q, k, v = make_qkv(2, H, n, d, dtype, seed=seed, H_kv=H_kv)
+        dout = make_dout(2, H, n, d, dtype, seed=seed)
+        _bwd_and_check(ea, oracle_lib, q, k, v, dout, causal, ea.default_scale(d),
+                       f"N={n} H={H} H_kv={H_kv} d={d} {dtype} causal={causal}")
+
+
+def test_bwd_scale_and_values(ea, oracle_lib):
+    """A non-default scale and larger scores (sharper softmax)."""
+    q, k, v = make_qkv(1, 2, 150, 64, torch.bfloat16, seed=9501, value_scale=2.0)
+    dout = make_dout(1, 2, 150, 64, torch.bfloat16, seed=9501)
+    _bwd_and_check(ea, oracle_lib, q, k, v, dout, True, 0.3, "scale 0.3, values x2")
+
+
+FULL = ["c3_bf16_causal", "g1_bf16_causal_gqa4", "c4_bf16_d128_causal"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_bwd_workload_full_size(ea, oracle_lib, name):
+    """Full-size workloads in the bench's launch configuration: every element
+    of the first and last K/V slices (the last only at d = 128; their query
+    heads' o and lse replaced by the oracle's), identities on every slice."""
+    w = WORKLOADS[name]
+    print(f"workload {name}: {w.describe()}", flush=True)
+    q, k, v = workload_inputs(w)
+    dout = workload_dout(w)
+    H_kv = w.kv_heads
+    G = w.H // H_kv
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, dout))
+    o, lse = ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    # The oracle needs ~15 s for one d = 128, N = 8192 slice: one slice there.
+    picks = [(w.B - 1, H_kv - 1)] if w.d == 128 else [(0, 0), (w.B - 1, H_kv - 1)]
+    subs = {}
+    for b, hk in picks:
+        hs = slice(hk * G, (hk + 1) * G)
+        sub = (q[b:b + 1, hs], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1],
+               dout[b:b + 1, hs])
+        sub = tuple(t.contiguous() for t in sub)
+        o_s, lse_s = _fwd_stats(oracle_lib, sub[0], sub[1], sub[2], w.causal, w.scale)
+        o[b, hs] = o_s[0].cuda()
+        lse[b, hs] = lse_s[0].cuda()
+        subs[(b, hk)] = sub
+    dq, dk, dv = ea.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    n_acc = G * w.N / 16 + 32
+    for (b, hk), sub in subs.items():
+        rq, rk, rv, eq, ek, ev, zq, zk, zv = oracle_lib.attn_bwd_ref(*sub, w.causal, w.scale,
+                                                                     error_scales=True)
+        hs = slice(hk * G, (hk + 1) * G)
+        tag = f"{name} slice b={b} h_kv={hk}"
+        _check(dq[b:b + 1, hs], rq, eq, zq, w.dtype, n_acc, tag + " dq")
+        _check(dk[b:b + 1, hk:hk + 1], rk, ek, zk, w.dtype, n_acc, tag + " dk")
+        _check(dv[b:b + 1, hk:hk + 1], rv, ev, zv, w.dtype, n_acc, tag + " dv")
+    # Identities on every slice: the keys' gradients sum to zero over keys;
+    # the values' gradients sum to the group's summed dout.
+    dk64 = dk.to(torch.float64)
+    dv64 = dv.to(torch.float64)
+    dsum = dod.to(torch.float64).reshape(w.B, H_kv, G, w.N, w.d).sum(dim=(2, 3))
+    tol_v = 4 * U[w.dtype] * dout.to(torch.float64).abs().reshape(
+        w.B, H_kv, G, w.N, w.d).sum(dim=(2, 3)).cuda() + 1e-3
+    assert torch.all((dv64.sum(dim=2) - dsum).abs() <= tol_v)
+    tol_k = 4 * U[w.dtype] * dk64.abs().sum(dim=2) + 1e-3
+    assert torch.all(dk64.sum(dim=2).abs() <= tol_k)
+
+
+def test_bwd_deterministic(ea):
+    """No atomics: repeated runs are bitwise identical."""
+    q, k, v = (t.cuda() for t in make_qkv(1, 4, 700, 64, torch.bfloat16, seed=5, H_kv=2))
+    dout = make_dout(1, 4, 700, 64, torch.bfloat16, seed=5).cuda()
+    o, lse = ea.fwd(q, k, v, causal=True)
+    a = ea.bwd(q, k, v, o, lse, dout, causal=True)
+    b = ea.bwd(q, k, v, o, lse, dout, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_composes_with_forward(ea, oracle_lib):
+    """The GPU forward's own o and lse as inputs: the gradients stay within
+    the bound widened by the forward's o error (up to the forward tolerance
+    2e-2 per element, which enters through D_i = dout_i . o_i)."""
+    dtype = torch.bfloat16
+    q, k, v = make_qkv(2, 4, 300, 64, dtype, seed=9601, H_kv=2)
+    dout = make_dout(2, 4, 300, 64, dtype, seed=9601)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, dout))
+    o, lse = ea.fwd(qd, kd, vd, causal=True)
+    dq, dk, dv = ea.bwd(qd, kd, vd, o, lse, dod, causal=True)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle_lib.attn_bwd_ref(q, k, v, dout, True, ea.default_scale(64))
+    o_ref, _ = oracle_lib.attn_fwd_ref(q, k, v, True, ea.default_scale(64))
+    o_err = np.abs(o.cpu().double().numpy() - o_ref).max()
+    assert o_err <= 2e-2
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        rel = np.abs(got.cpu().double().numpy() - ref).max() / np.abs(ref).max()
+        print(f"composed: rel max-abs {rel:.3e} (o err {o_err:.2e})", flush=True)
+        assert rel <= 4e-2

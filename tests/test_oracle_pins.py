@@ -456,6 +456,156 @@ def test_gqa_rejects_bad_head_counts(orc):
         orc.attn_fwd_ref(q, k[:, :2], v[:, :1], False, 1.0)   # k, v shapes differ
 
 
+# ---------------------------------------------------------- backward
+# The pages name the backward pass without formulas ('Flash Attention v2 的核心
+# 优化原理与工程实现', comparison section); the oracle's gradient is the chain
+# rule of the forward definition. Pinned to torch's fp64 autograd (a library
+# routine), to central differences of the oracle's own forward, and to
+# identities every correct gradient satisfies.
+
+def _autograd_grads(q, k, v, dout, causal, scale):
+    qq, kk, vv = (t.to(torch.float64).requires_grad_() for t in (q, k, v))
+    G = q.shape[1] // k.shape[1]
+    ke, ve = kk.repeat_interleave(G, dim=1), vv.repeat_interleave(G, dim=1)
+    s = float(scale) * torch.matmul(qq, ke.transpose(-1, -2).contiguous())
+    if causal:
+        n = s.shape[-1]
+        s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), diagonal=1), float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), ve)
+    o.backward(dout.to(torch.float64))
+    return qq.grad.numpy(), kk.grad.numpy(), vv.grad.numpy()
+
+
+def _grads_inputs(B, H, H_kv, N, d, dtype, seed):
+    q, k, v = make_qkv(B, H, N, d, dtype, seed=seed, H_kv=H_kv)
+    g = torch.Generator().manual_seed(seed + 1)
+    dout = torch.randn(B, H, N, d, generator=g).to(dtype)
+    return q, k, v, dout
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (4, 2), (3, 1)])
+def test_bwd_matches_autograd(orc, dtype, causal, H, H_kv):
+    q, k, v, dout = _grads_inputs(2, H, H_kv, 11, 8, dtype, seed=50 + H + H_kv)
+    dq, dk, dv = orc.attn_bwd_ref(q, k, v, dout, causal, 0.375)
+    rq, rk, rv = _autograd_grads(q, k, v, dout, causal, 0.375)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_bwd_central_differences_of_forward(orc):
+    """dL/dx for L = sum(O * dout), by central differences of the oracle's own
+    forward with exactly representable fp32 steps."""
+    g = torch.Generator().manual_seed(61)
+    B, H, N, d = 1, 1, 6, 4
+    q, k, v = (torch.randint(-8, 9, (B, H, N, d), generator=g).to(torch.float32) / 8
+               for _ in range(3))
+    dout = torch.randint(-4, 5, (B, H, N, d), generator=g).to(torch.float32) / 4
+    for causal in (False, True):
+        dq, dk, dv = orc.attn_bwd_ref(q, k, v, dout, causal, 0.5)
+        h = 2.0 ** -12
+
+        def loss(qx, kx, vx):
+            o, _ = orc.attn_fwd_ref(qx, kx, vx, causal, 0.5)
+            return float((o * dout.double().numpy()).sum())
+        for which, grad in ((0, dq), (1, dk), (2, dv)):
+            for idx in [(0, 0, 0, 0), (0, 0, 2, 1), (0, 0, 5, 3), (0, 0, 3, 2)]:
+                xs = [q.clone(), k.clone(), v.clone()]
+                xs[which][idx] += h
+                lp = loss(*xs)
+                xs[which][idx] -= 2 * h
+                lm = loss(*xs)
+                fd = (lp - lm) / (2 * h)
+                assert abs(fd - grad[idx]) <= 1e-6 * (1 + abs(grad[idx])), (which, idx, fd, grad[idx])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_identities(orc, causal):
+    """Softmax rows are shift invariant, so sum_j ds_ij = 0 and the keys'
+    gradients sum to zero; rows of P sum to one, so the values' gradients sum
+    to the group's summed dout; the error scales dominate the gradients."""
+    q, k, v, dout = _grads_inputs(2, 4, 2, 37, 16, torch.bfloat16, seed=70)
+    dq, dk, dv, eq, ek, ev, zq, zk, zv = orc.attn_bwd_ref(q, k, v, dout, causal, 0.25,
+                                                          error_scales=True)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    g = _f64(dout).reshape(2, 2, 2, 37, 16).sum(axis=(2, 3))   # [B, H_kv, d]
+    np.testing.assert_allclose(dv.sum(axis=2), g, rtol=1e-12, atol=1e-12)
+    for grad, e in ((dq, eq), (dk, ek), (dv, ev)):
+        assert np.all(e >= np.abs(grad) * (1 - 1e-12))
+    # the absolute-rounding scales of dv count each visible row's |dout| once
+    da = np.abs(_f64(dout)).reshape(2, 2, 2, 37, 16)
+    if causal:
+        cnt = np.flip(np.cumsum(np.flip(da, axis=3), axis=3), axis=3).sum(axis=2)
+    else:
+        cnt = np.broadcast_to(da.sum(axis=(2, 3))[:, :, None, :], zv.shape)
+    np.testing.assert_allclose(zv, cnt, rtol=1e-12)
+    assert np.all(zk >= 0) and np.all(zq >= 0)
+
+
+def test_bwd_special_cases(orc):
+    # N = 1: o = v, so dv = dout and dq = dk = 0
+    q, k, v, dout = _grads_inputs(1, 2, 2, 1, 8, torch.float32, seed=80)
+    dq, dk, dv = orc.attn_bwd_ref(q, k, v, dout, True, 0.5)
+    np.testing.assert_array_equal(dq, 0.0)
+    np.testing.assert_array_equal(dk, 0.0)
+    np.testing.assert_allclose(dv, _f64(dout), rtol=0, atol=0)
+    # constant V: o does not depend on q or k
+    q, k, v, dout = _grads_inputs(1, 2, 1, 20, 8, torch.bfloat16, seed=81)
+    v = torch.full_like(v, 0.75)
+    for causal in (False, True):
+        dq, dk, dv = orc.attn_bwd_ref(q, k, v, dout, causal, 0.5)
+        assert np.abs(dq).max() < 1e-13 and np.abs(dk).max() < 1e-13
+
+
+def test_bwd_linear_in_dout(orc):
+    q, k, v, d1 = _grads_inputs(1, 2, 1, 19, 8, torch.float32, seed=90)
+    g = torch.Generator().manual_seed(91)
+    d2 = torch.randint(-4, 5, d1.shape, generator=g).to(torch.float32) / 4
+    d1 = torch.randint(-4, 5, d1.shape, generator=g).to(torch.float32) / 4
+    a = orc.attn_bwd_ref(q, k, v, d1, True, 0.5)
+    b = orc.attn_bwd_ref(q, k, v, d2, True, 0.5)
+    c = orc.attn_bwd_ref(q, k, v, d1 + d2, True, 0.5)
+    for x, y, z in zip(a, b, c):
+        np.testing.assert_allclose(x + y, z, rtol=1e-12, atol=1e-13)
+
+
+def test_bwd_causal_key_sees_only_later_rows(orc):
+    """Under the causal mask key j only receives gradient from rows i >= j:
+    changing dout rows < r leaves dk, dv of keys >= r unchanged."""
+    q, k, v, dout = _grads_inputs(1, 2, 2, 30, 8, torch.float32, seed=95)
+    r = 17
+    d2 = dout.clone()
+    d2[:, :, :r] = torch.randn(1, 2, r, 8)
+    a = orc.attn_bwd_ref(q, k, v, dout, True, 0.5)
+    b = orc.attn_bwd_ref(q, k, v, d2, True, 0.5)
+    np.testing.assert_array_equal(a[1][:, :, r:], b[1][:, :, r:])
+    np.testing.assert_array_equal(a[2][:, :, r:], b[2][:, :, r:])
+    np.testing.assert_array_equal(a[0][:, :, r:], b[0][:, :, r:])   # dq rows >= r too
+    assert not np.array_equal(a[1][:, :, :r], b[1][:, :, :r])
+
+
+def test_bwd_gqa_sums_expanded_heads(orc):
+    q, k, v, dout = _grads_inputs(2, 6, 2, 15, 8, torch.float16, seed=99)
+    G = 3
+    ke = k.repeat_interleave(G, dim=1).contiguous()
+    ve = v.repeat_interleave(G, dim=1).contiguous()
+    dq, dk, dv = orc.attn_bwd_ref(q, k, v, dout, True, 0.5)
+    eq_, ek_, ev_ = orc.attn_bwd_ref(q, ke, ve, dout, True, 0.5)
+    np.testing.assert_array_equal(dq, eq_)
+    np.testing.assert_allclose(dk, ek_.reshape(2, 2, 3, 15, 8).sum(axis=2), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dv, ev_.reshape(2, 2, 3, 15, 8).sum(axis=2), rtol=1e-13, atol=1e-14)
+
+
+def test_bwd_thread_count_does_not_change_result(orc):
+    q, k, v, dout = _grads_inputs(1, 2, 1, 40, 8, torch.bfloat16, seed=97)
+    a = orc.attn_bwd_ref(q, k, v, dout, False, 0.5, num_threads=1)
+    b = orc.attn_bwd_ref(q, k, v, dout, False, 0.5, num_threads=5)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(a[2], b[2], rtol=1e-13, atol=1e-15)
+
+
 # ------------------------------------------------------------ errors
 
 def test_oracle_rejects_bad_arguments(orc):
