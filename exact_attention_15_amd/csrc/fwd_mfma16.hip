@@ -125,14 +125,14 @@ __device__ __forceinline__ void tile_src_offsets(int cw, int lane, int* off) {
 }
 
 // This copy-wave's share of the HBM -> LDS copy of one K or V tile (keys
-// kv0 .. kv0+63). The buffer descriptor covers rows kv0 .. N-1 only, so
+// kv0 .. kv0+63). The buffer descriptor covers rows kv0 .. min(N, kv0+64)-1, so
 // chunks of rows past N are out of range and arrive as zeros (the zero-fill
 // of the pages' asynchronous copy); their scores are masked.
 template <int D>
 __device__ __forceinline__ void copy_tile(const uint16_t* g_slice, int kv0, int N, LDS_AS char* buf,
                                           int cw, const int* off) {
     using T = Tile<D>;
-    const int rows = max(N - kv0, 0);
+    const int rows = min(max(N - kv0, 0), kBlockN);   // one tile: the range cannot overflow
     const i32x4 rsrc = buffer_rsrc(g_slice + (size_t)kv0 * D, rows * T::kRowBytes);
     const uint32_t lds0 = (uint32_t)(uintptr_t)buf;
 #pragma unroll
