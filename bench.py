@@ -8,6 +8,9 @@ Prints ONE JSON line with the attention TFLOPS, its roofline fraction and
 the CPU fp64 oracle timed on a bounded sample of the same workload.
 ``--pass bwd`` times the backward pass (dQ, dK, dV) instead: one step is one
 attn_bwd call (its three kernels) with q, k, v, o, lse and dO resident.
+``--pass unfused`` times the unfused three-kernel forward (S, softmax, P V
+with N x N buffers) and, on the same inputs, the fused kernel, and reports
+what fusion gains.
 
 FLOP convention (every page's): 4*B*H*N^2*d per forward, halved for causal —
 checked against the figures printed in "Flash Attention（二）v2版本朴素实现
@@ -217,6 +220,94 @@ def run_bwd(args, name, w):
     print(json.dumps(line), flush=True)
 
 
+def _time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps, time.perf_counter() - t_wall
+
+
+def run_unfused(args, name, w):
+    """Unfused-versus-fused comparison line (``--pass unfused``)."""
+    import numpy as np
+    import torch
+
+    import exact_attention_15_amd as ea
+    from exact_attention_15_amd.inputs import workload_inputs
+
+    dt_name = DTYPE_NAME[str(w.dtype)]
+    if dt_name == "fp32":
+        print("bench.py: the unfused path takes fp16 / bf16 inputs", file=sys.stderr)
+        sys.exit(2)
+    ea.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = workload_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    ws = torch.empty(ea.unfused_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+    o, lse = ea.fwd_unfused(qd, kd, vd, causal=w.causal, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    parity = None
+    if not args.no_check:
+        import oracle
+        rng = np.random.default_rng(1)
+        rows = np.unique(np.concatenate([np.arange(8), rng.integers(0, w.B * w.H * w.N, 56)]))
+        o_ref, _ = oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows)
+        parity = float(np.abs(o.cpu().double().numpy().reshape(-1, w.d)[rows] - o_ref).max())
+        if not parity <= 2e-2:
+            print(f"bench.py: unfused parity gate failed: {parity:.3e}", file=sys.stderr)
+            sys.exit(1)
+    steps = max(1, args.steps // 10)
+    ms_u, t_wall = _time_calls(lambda: ea.fwd_unfused(qd, kd, vd, causal=w.causal,
+                                                      scale=w.scale, workspace=ws),
+                               steps, max(1, args.warmup // 10))
+    out = (torch.empty_like(qd), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev))
+    ms_f, _ = _time_calls(lambda: ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out),
+                          args.steps, args.warmup)
+    flops = attention_flops(w.B, w.H, w.N, w.d, w.causal)
+    tflops = flops / (ms_u * 1e-3) / 1e12
+    ld = (w.N + 63) // 64 * 64
+    # The method's own traffic: S written and read (fp32), P written and read
+    # (16-bit), plus Q, K, V read and O, lse written.
+    mbytes = w.B * w.H * w.N * ld * (4 + 4 + 2 + 2) + algorithmic_bytes(w.B, w.H, w.N, w.d, 2)
+    gbs = mbytes / (ms_u * 1e-3) / 1e9
+    line = {
+        "metric": "unfused attention fwd TFLOPS (S, softmax, P V as three kernels)",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(1, args.warmup // 10),
+        "ms_per_step": round(ms_u, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name,
+        "data": "synthetic (seeded i.i.d. N(0,1) inputs rounded to the dtype)",
+        "config": {"workload": w.describe() + " (unfused)", "name": name, "B": w.B, "H": w.H,
+                   "N": w.N, "d": w.d, "causal": w.causal, "scale": w.scale},
+        # The unfused path is bound by its N x N traffic.
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "fused_ms_per_step": round(ms_f, 5),
+        "fused_tflops": round(flops / (ms_f * 1e-3) / 1e12, 2),
+        "fusion_speedup": round(ms_u / ms_f, 2),
+        "parity_o_max_abs_sampled": parity,
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,8 +316,9 @@ def main():
     # its sustained clocks; fewer warm-up launches time a ramping clock.
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd",
-                    help="time the forward (default) or the backward pass")
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "unfused"], default="fwd",
+                    help="time the forward (default), the backward pass, or the unfused "
+                         "forward against the fused one")
     ap.add_argument("--cpu-slices", type=int, default=None,
                     help="slices the CPU oracle baseline runs on: (b,h) slices for the forward "
                          "(default 64), K/V slices for the backward (default 4)")
@@ -262,6 +354,9 @@ def main():
     w = WORKLOADS[name]
     if args.pass_ == "bwd":
         run_bwd(args, name, w)
+        return
+    if args.pass_ == "unfused":
+        run_unfused(args, name, w)
         return
     dt_name = DTYPE_NAME[str(w.dtype)]
     ea.load_library()

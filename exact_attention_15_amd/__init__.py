@@ -47,6 +47,11 @@ def load_library():
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                              ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                     ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_fwd_unfused.restype = ctypes.c_int
+    lib.attn_unfused_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_unfused_workspace_bytes.restype = i64
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -193,5 +198,49 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     return dq, dk, dv
 
 
-__all__ = ["fwd", "bwd", "attn_bwd", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
+def attn_fwd_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, causal, scale,
+                     dtype, stream) -> int:
+    """Raw C-ABI call of the unfused three-kernel forward."""
+    return load_library().attn_fwd_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, N,
+                                           d, int(causal), float(scale), int(dtype), stream)
+
+
+def unfused_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load_library().attn_unfused_workspace_bytes(B, H, N))
+
+
+def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, workspace=None):
+    """The unfused forward (S, softmax, P V as three kernels with N x N
+    buffers): the comparison path. Returns (o, lse) like ``fwd``.
+    ``workspace`` may pass a preallocated uint8 device tensor of at least
+    ``unfused_workspace_bytes(B, H, N)`` bytes."""
+    import torch
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if t.device.type != "cuda" or t.device != q.device or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous tensors on one GPU device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    need = unfused_workspace_bytes(B, H, N)
+    if need < 0:
+        raise ValueError("sizes out of range")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N,
+                              d, causal, scale, dtype_code(q.dtype), stream)
+    if rc != ATTN_OK:
+        raise AttnError(rc, strerror(rc))
+    return o, lse
+
+
+__all__ = ["fwd", "bwd", "fwd_unfused", "attn_fwd_unfused", "unfused_workspace_bytes", "attn_bwd", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
            "dtype_code", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["attn_api.hip", "fwd_mfma16.hip", "fwd_f32.hip", "bwd_mfma16.hip"]
+SOURCES = ["attn_api.hip", "fwd_mfma16.hip", "fwd_f32.hip", "bwd_mfma16.hip", "unfused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

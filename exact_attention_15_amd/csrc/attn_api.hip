@@ -103,6 +103,45 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+extern "C" int64_t attn_unfused_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+    if (B < 1 || H < 1 || N < 1 || N > (int64_t)INT32_MAX - 64) return -1;
+    const int64_t ld = (N + 63) / 64 * 64;
+    if (B > INT64_MAX / H || B * H > INT64_MAX / N || B * H * N > INT64_MAX / ld / 8) return -1;
+    return B * H * N * ld * 6;   // fp32 scores + 16-bit probabilities
+}
+
+extern "C" int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
+                                void* workspace, int64_t workspace_bytes, int64_t B, int64_t H,
+                                int64_t N, int64_t d, int causal, float scale, int dtype,
+                                void* stream) {
+    const int rc = validate(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (!workspace) return ATTN_EINVAL;
+    const int64_t need = attn_unfused_workspace_bytes(B, H, N);
+    if (need < 0 || workspace_bytes < need) return ATTN_EINVAL;
+    const int64_t nt = (N + 63) / 64;
+    if (B * H > (int64_t)INT32_MAX / nt / nt) return ATTN_EINVAL;   // one-dimensional grid
+    if (dtype == ATTN_F32) return ATTN_EUNSUPPORTED;
+    if (((uintptr_t)workspace & 255u) != 0) return ATTN_EALIGN;
+
+    attn::UnfusedParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.N = N;
+    p.ld = nt * 64;
+    p.BH = (int)(B * H);
+    p.causal = causal;
+    p.scale = scale;
+    p.s = (float*)workspace;
+    p.pm = (char*)workspace + B * H * N * p.ld * 4;
+    (void)hipGetLastError();
+    const hipError_t e = attn::launch_unfused16(p, dtype == ATTN_BF16, (int)d, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                         int dtype, void* stream) {
@@ -113,8 +152,8 @@ extern "C" const char* attn_strerror(int code) {
     switch (code) {
         case ATTN_OK: return "ok";
         case ATTN_EINVAL: return "invalid argument (pointer, size, H_kv, dtype, scale or causal)";
-        case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128), or fp32 in attn_bwd";
-        case ATTN_EALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+        case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128), or fp32 in attn_bwd / attn_fwd_unfused";
+        case ATTN_EALIGN: return "a tensor pointer is misaligned (16 bytes; lse, delta 4; workspace 256)";
         case ATTN_EHIP: return "HIP kernel launch failed";
         default: return "unknown error code";
     }

@@ -62,6 +62,22 @@ struct BwdParams {
     float scale_log2;   // scale * log2(e)
 };
 
+// Unfused three-step forward (the materialised comparison path).
+struct UnfusedParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    float* s;           // [B*H, N, ld] fp32 scores (workspace)
+    void* pm;           // [B*H, N, ld] probabilities in the input type (workspace)
+    int64_t N;
+    int64_t ld;         // row stride of s and pm: N rounded up to 64
+    int BH;
+    int causal;
+    float scale;
+};
+
 // Query rows per workgroup for every kernel here.
 constexpr int kBlockM = 128;
 
@@ -69,5 +85,6 @@ constexpr int kBlockM = 128;
 hipError_t launch_fwd16(const FwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s);
 hipError_t launch_fwd32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd16(const BwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s);
+hipError_t launch_unfused16(const UnfusedParams& p, bool is_bf16, int d, hipStream_t s);
 
 }  // namespace attn

@@ -59,89 +59,6 @@ constexpr int kQStage = 64;                   // query rows per LDS stage (dK/dV
 constexpr int kQueryBlock = kBwdWaves * 32;   // query rows per dQ workgroup
 constexpr int kKStage = 64;                   // keys per LDS stage (dQ kernel)
 
-// A ROWS x D tile of 16-bit values in LDS, row-major, 16-byte chunk c of
-// row r stored at chunk c ^ swz(r). The tile is read two ways:
-//  * by rows: 16 bytes per lane, lanes 0-15 at rows 0-15 and one logical
-//    chunk; needs rows 0-15 in 16 different 16-byte bank groups;
-//  * by ds_read_b64_tr_b16: 32 lanes read 4 consecutive rows (4m .. 4m+3)
-//    x 64 bytes (an aligned block of 4 chunks); needs the 4 rows' blocks in
-//    4 different places.
-// d = 64 (two rows per 256-byte bank row): swz takes bits 1-3 of r so that
-// rows of one parity get 8 different values, with rows r and r+2 differing
-// in bit 2 (the 64-byte half). d = 128: swz swaps the two low bit pairs of
-// r, a permutation of 0-15 whose bits 2-3 differ across 4 aligned rows.
-template <int ROWS, int D>
-struct BTile {
-    static constexpr int kRowBytes = D * 2;
-    static constexpr int kChunks = D / 8;
-    static constexpr int kBytes = ROWS * kRowBytes;
-    static __device__ __forceinline__ int swz(int r) {
-        return D == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
-                       : (((r & 3) << 2) | ((r >> 2) & 3));
-    }
-    // Row read: row r, logical chunk c.
-    static __device__ __forceinline__ int row_off(int r, int c) {
-        return r * kRowBytes + ((c ^ swz(r)) << 4);
-    }
-};
-
-// HBM -> LDS copy of one ROWS x D tile by NW waves (16 bytes per lane per
-// copy). Copy u of wave cw fills LDS chunk slots s = (cw*U + u)*64 + lane,
-// i.e. row s / kChunks, physical chunk s % kChunks, with the global chunk
-// (physical ^ swz(row)). Rows past N are outside the buffer range: zeros.
-template <int ROWS, int D, int NW>
-struct BCopy {
-    using T = BTile<ROWS, D>;
-    static constexpr int kPerWave = T::kBytes / 1024 / NW;
-    static_assert(kPerWave >= 1 && T::kBytes % (1024 * NW) == 0, "tile / copy waves mismatch");
-    static __device__ __forceinline__ void offsets(int cw, int lane, int* off) {
-#pragma unroll
-        for (int u = 0; u < kPerWave; ++u) {
-            const int s = (cw * kPerWave + u) * 64 + lane;
-            const int r = s / T::kChunks;
-            const int pc = s % T::kChunks;
-            off[u] = r * T::kRowBytes + ((pc ^ T::swz(r)) << 4);
-        }
-    }
-    static __device__ __forceinline__ void copy(const uint16_t* g_slice, int row0, int N,
-                                                LDS_AS char* buf, int cw, const int* off) {
-        const int rows = min(max(N - row0, 0), ROWS);
-        const i32x4 rsrc = buffer_rsrc(g_slice + (size_t)row0 * D, rows * T::kRowBytes);
-        const uint32_t lds0 = (uint32_t)(uintptr_t)buf;
-#pragma unroll
-        for (int u = 0; u < kPerWave; ++u)
-            dma16(rsrc, lds0 + (cw * kPerWave + u) * 64 * 16, off[u]);
-    }
-};
-
-// Offsets of the ds_read_b64_tr_b16 reads that build a 32x32x16 A operand
-// X^T[d][row] from a row-major tile X: in each group of 16 lanes, output
-// lane j receives element j%4 of the 8-byte reads of source lanes j/4 + 4k.
-// Source lane (G = lane/16, i = lane%16) reads row 4g + i/4 + 8h (+16 kb2)
-// at columns 32 db + 16 (G%2) + 4 (i%4), so output lane l holds
-// X[16 kb2 + 8h + 4g + k][32 db + l%32], k = 0..3, h = 0 (first read) or 1
-// (second): the row order of the 32x32 accumulator's entries. The swizzle
-// depends on row bit 3, hence one offset per h.
-template <int ROWS, int D>
-__device__ __forceinline__ void tr_offsets(int lane, int (*off)[2]) {
-    using T = BTile<ROWS, D>;
-    const int g = lane >> 5, G = lane >> 4, i16 = lane & 15;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 4 * g + (i16 >> 2) + 8 * h;
-            const int col = 32 * db + 16 * (G & 1) + 4 * (i16 & 3);
-            off[db][h] = row * T::kRowBytes + (((col >> 3) ^ T::swz(row)) << 4) + ((col >> 2) & 1) * 8;
-        }
-}
-
-__device__ __forceinline__ u32x4 tr_read(const LDS_AS char* p0, const LDS_AS char* p1) {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p0);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p1);
-    return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 // 16-bit value to fp32.
 template <bool IS_BF16>
 __device__ __forceinline__ float lo16(uint32_t w) {

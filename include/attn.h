@@ -9,7 +9,8 @@
  * Sources (cited by page title and section):
  *   [naive-attn]  cishoon.github.io, "flashattention" post, section 1.1.2:
  *                 the attention formula, the 1/sqrt(d) scaling (item 2) and
- *                 the row-wise safe softmax (item 3).
+ *                 the row-wise safe softmax (item 3); sections 2-3: the
+ *                 unfused three-kernel method (attn_fwd_unfused).
  *   [v2-naive]    "Flash Attention（二）v2版本朴素实现 cuda core":
  *                 section 1.1 (Q-tile outer loop, K/V-tile inner loop),
  *                 1.2 (row max m and row sum l kept on chip), 1.3 (deferred
@@ -38,8 +39,9 @@ typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
 enum {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,       /* bad argument (null pointer, size, H_kv, dtype, scale, causal) */
-    ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128; fp32 in attn_bwd */
-    ATTN_EALIGN = -3,       /* a base pointer not 16-byte aligned */
+    ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128; fp32 in attn_bwd or
+                               attn_fwd_unfused */
+    ATTN_EALIGN = -3,       /* a base pointer misaligned (see each function) */
     ATTN_EHIP = -4          /* the HIP launch failed */
 };
 
@@ -136,6 +138,32 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, void* dq, void* dk, void* dv, float* delta,
              int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int causal,
              float scale, int dtype, void* stream);
+
+/*
+ * attn_fwd_unfused — the same forward pass (multi-head, H_kv = H) computed
+ * the unfused way, one kernel per step with the N x N matrices in memory:
+ * S = scale Q K^T (fp32), a row softmax into P (rounded to `dtype`) and lse,
+ * then O = P V. This is the materialised three-kernel method of [naive-attn]
+ * sections 2-3, kept as the baseline that shows what fusion gains; under
+ * causal = 1 the full S is computed and the softmax gives the keys j > i
+ * probability 0.
+ *
+ * q, k, v, o, lse, B, H, N, d, causal, scale, stream: as for attn_fwd.
+ * dtype        ATTN_F16 or ATTN_BF16 (fp32: ATTN_EUNSUPPORTED).
+ * workspace    DEVICE pointer, 256-byte aligned, of workspace_bytes >=
+ *              attn_unfused_workspace_bytes(B, H, N) bytes, owned by the
+ *              caller; overwritten (S and P, rows padded to a multiple of 64
+ *              columns). Too small or NULL: ATTN_EINVAL.
+ * Asynchronous on `stream`, allocates nothing; validation precedes any HIP
+ * call.
+ */
+int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                     int64_t d, int causal, float scale, int dtype, void* stream);
+
+/* attn_unfused_workspace_bytes — bytes of workspace attn_fwd_unfused needs:
+ * B*H*N*ld*6 with ld = N rounded up to 64; -1 for sizes out of range. */
+int64_t attn_unfused_workspace_bytes(int64_t B, int64_t H, int64_t N);
 
 /* attn_strerror — static description of a return code (never NULL). */
 const char* attn_strerror(int code);

@@ -45,7 +45,8 @@ def test_every_header_is_covered():
 
 def test_attn_library_exports_header(attn_lib_path):
     decl = _declared_functions("attn.h")
-    assert decl == ["attn_bwd", "attn_fwd", "attn_fwd_gqa", "attn_strerror"]
+    assert decl == ["attn_bwd", "attn_fwd", "attn_fwd_gqa", "attn_fwd_unfused", "attn_strerror",
+                    "attn_unfused_workspace_bytes"]
     missing = set(decl) - _exported(attn_lib_path)
     assert not missing, missing
     ctypes.CDLL(attn_lib_path)   # loads without a GPU
@@ -162,6 +163,37 @@ def test_bwd_argument_validation(attn_lib_path):
     for change, want in cases:
         a = dict(good, **change)
         rc = ea.attn_bwd(*(a[n] for n in names))
+        assert rc == want, (change, rc)
+
+
+def test_unfused_workspace_and_validation(attn_lib_path):
+    import exact_attention_15_amd as ea
+    assert ea.unfused_workspace_bytes(1, 1, 1) == 64 * 6
+    assert ea.unfused_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 128 * 6
+    assert ea.unfused_workspace_bytes(4, 16, 4096) == 4 * 16 * 4096 * 4096 * 6
+    for bad in [(0, 1, 1), (1, -1, 4), (1, 1, 0)]:
+        assert ea.unfused_workspace_bytes(*bad) == -1
+    P = 0x7f0000000000
+    need = ea.unfused_workspace_bytes(1, 2, 128)
+    good = dict(q=P, k=P + 0x1000, v=P + 0x2000, o=P + 0x3000, lse=P + 0x4000,
+                ws=P + 0x10000, wsb=need, B=1, H=2, N=128, d=64, causal=1, scale=0.125,
+                dtype=ea.ATTN_BF16, stream=None)
+    cases = [
+        (dict(ws=None), ea.ATTN_EINVAL),
+        (dict(wsb=need - 1), ea.ATTN_EINVAL),
+        (dict(q=None), ea.ATTN_EINVAL),
+        (dict(N=0), ea.ATTN_EINVAL),
+        (dict(causal=3), ea.ATTN_EINVAL),
+        (dict(dtype=ea.ATTN_F32), ea.ATTN_EUNSUPPORTED),
+        (dict(d=32), ea.ATTN_EUNSUPPORTED),
+        (dict(ws=P + 0x10080), ea.ATTN_EALIGN),
+        (dict(o=P + 0x3008), ea.ATTN_EALIGN),
+    ]
+    names = ["q", "k", "v", "o", "lse", "ws", "wsb", "B", "H", "N", "d", "causal", "scale",
+             "dtype", "stream"]
+    for change, want in cases:
+        a = dict(good, **change)
+        rc = ea.attn_fwd_unfused(*(a[n] for n in names))
         assert rc == want, (change, rc)
 
 
