@@ -22,7 +22,8 @@
 //     of scheduling: (1) D per row into the caller's fp32 `delta` buffer;
 //     (2) dK, dV: a workgroup owns 128 keys of one K/V head (32 per wave, its
 //     K and V fragments held in VGPRs) and streams every query tile that can
-//     see them, of every query head in the group, through LDS; (3) dQ: a
+//     see them, of every query head in the group, through LDS, two groups of
+//     waves taking alternate tiles; (3) dQ: a
 //     workgroup owns 128 query rows (32 per wave, Q and dO held in VGPRs) and
 //     streams the K/V tiles. dQ is thus recomputed from S rather than summed
 //     across the dK/dV workgroups: one more product instead of a
@@ -97,40 +98,60 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_delta_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // (2) dK, dV. Work item: (key tile of 128, b*H_kv + h_kv). Causal items are
-// ordered key tile 0 first: it is seen by the most query rows.
-template <bool IS_BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
+// ordered key tile 0 first: it is seen by the most query rows. The item's
+// query steps (every query tile of every query head of the group that can
+// see the keys) are dealt round-robin to GROUPS groups of 4 waves, each with
+// its own LDS stage buffers and its own partial dK, dV for the same 128
+// keys; the partials are summed through LDS at the end. Two groups halve the
+// sequential length of an item at no extra traffic; they are used for
+// grouped-query heads at d = 64, where an item spans G heads and the items
+// are G times fewer. (With one query head per item, two 4-wave workgroups
+// per CU keep more independent work in flight than one 8-wave workgroup;
+// at d = 128 the registers do not hold a second group's waves.)
+template <bool IS_BF16, int D, bool CAUSAL, int GROUPS>
+__global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdParams p) {
     using Op = Op16<IS_BF16>;
     using T = BTile<kQStage, D>;
     using Cp = BCopy<kQStage, D, kBwdWaves>;
     constexpr int NKD = D / 16;   // contraction steps over d
     constexpr int NDB = D / 32;   // 32-row blocks of dK^T / dV^T
 
-    __shared__ __attribute__((aligned(1024))) char q_lds0[T::kBytes];
-    __shared__ __attribute__((aligned(1024))) char q_lds1[T::kBytes];
-    __shared__ __attribute__((aligned(1024))) char o_lds0[T::kBytes];   // dO
-    __shared__ __attribute__((aligned(1024))) char o_lds1[T::kBytes];
-    __shared__ __attribute__((aligned(16))) float l_lds0[kQStage];      // lse * log2(e)
-    __shared__ __attribute__((aligned(16))) float l_lds1[kQStage];
-    __shared__ __attribute__((aligned(16))) float d_lds0[kQStage];      // -D
-    __shared__ __attribute__((aligned(16))) float d_lds1[kQStage];
-    LDS_AS char* const qL[2] = {(LDS_AS char*)q_lds0, (LDS_AS char*)q_lds1};
-    LDS_AS char* const oL[2] = {(LDS_AS char*)o_lds0, (LDS_AS char*)o_lds1};
-    LDS_AS float* const lL[2] = {(LDS_AS float*)l_lds0, (LDS_AS float*)l_lds1};
-    LDS_AS float* const dL[2] = {(LDS_AS float*)d_lds0, (LDS_AS float*)d_lds1};
+    // Per parity, one tile per group: Q, dO, lse * log2(e) and -D. After the
+    // loop the Q and dO space holds group 1's partial sums.
+    static_assert(GROUPS == 1 || 4 * GROUPS * T::kBytes >= 2 * NDB * 16 * kBwdThreads * 4,
+                  "reduction space");
+    static_assert(GROUPS <= 2, "one partial-sum hand-over");
+    __shared__ __attribute__((aligned(1024))) char q_lds0[GROUPS * T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char q_lds1[GROUPS * T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char o_lds0[GROUPS * T::kBytes];   // dO
+    __shared__ __attribute__((aligned(1024))) char o_lds1[GROUPS * T::kBytes];
+    __shared__ __attribute__((aligned(16))) float l_lds0[GROUPS * kQStage];      // lse * log2(e)
+    __shared__ __attribute__((aligned(16))) float l_lds1[GROUPS * kQStage];
+    __shared__ __attribute__((aligned(16))) float d_lds0[GROUPS * kQStage];      // -D
+    __shared__ __attribute__((aligned(16))) float d_lds1[GROUPS * kQStage];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = GROUPS == 1 ? 0 : wave >> 2;   // step group
+    const int wk = wave & 3;                     // key block of this wave
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int g = lane >> 5;
     const int N = (int)p.N;
+    LDS_AS char* const qL[2] = {(LDS_AS char*)q_lds0 + grp * T::kBytes,
+                                (LDS_AS char*)q_lds1 + grp * T::kBytes};
+    LDS_AS char* const oL[2] = {(LDS_AS char*)o_lds0 + grp * T::kBytes,
+                                (LDS_AS char*)o_lds1 + grp * T::kBytes};
+    LDS_AS float* const lL[2] = {(LDS_AS float*)l_lds0 + grp * kQStage,
+                                 (LDS_AS float*)l_lds1 + grp * kQStage};
+    LDS_AS float* const dL[2] = {(LDS_AS float*)d_lds0 + grp * kQStage,
+                                 (LDS_AS float*)d_lds1 + grp * kQStage};
 
     const int w = blockIdx.x;
     const int kt = w / p.BH_kv;
     const int kv_bh = w - kt * p.BH_kv;
     const int k0 = kt * kKeyBlock;
-    const int kw = k0 + 32 * wave;               // first key of this wave
+    const int kw = k0 + 32 * wk;                 // first key of this wave
     const int key = kw + l32;                    // this lane's key
     const size_t kv_base = (size_t)kv_bh * (size_t)N * D;
     // Query heads of this K/V head: bh0 .. bh0 + G - 1 (b*H + h_kv*G + g).
@@ -160,12 +181,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
     int troff[NDB][2];
     tr_offsets<kQStage, D>(lane, troff);
     int coff[Cp::kPerWave];
-    Cp::offsets(wave, lane, coff);
+    Cp::offsets(wk, lane, coff);
 
     const int n_qt = (N + kQStage - 1) / kQStage;
     const int t0 = CAUSAL ? k0 / kQStage : 0;    // first query tile that sees these keys
     const int n_t = n_qt - t0;
     const int n_steps = p.G * n_t;
+    const int n_iter = (n_steps + GROUPS - 1) / GROUPS;   // steps GROUPS*i + grp
     const float c2 = p.scale_log2;
 
     f32x16 dk[NDB], dv[NDB];
@@ -183,9 +205,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
         const int hh = s / n_t;
         const int t = t0 + (s - hh * n_t);
         const size_t base = (size_t)(bh0 + hh) * (size_t)N;
-        Cp::copy((const uint16_t*)p.q + base * D, t * kQStage, N, qbuf, wave, coff);
-        Cp::copy((const uint16_t*)p.dout + base * D, t * kQStage, N, obuf, wave, coff);
-        if (wave == 0) {
+        Cp::copy((const uint16_t*)p.q + base * D, t * kQStage, N, qbuf, wk, coff);
+        Cp::copy((const uint16_t*)p.dout + base * D, t * kQStage, N, obuf, wk, coff);
+        if (wk == 0) {
             const int row = t * kQStage + lane;
             // Rows past N: P = exp2(-inf) = 0, so they contribute nothing.
             nl = row < N ? p.lse[base + row] * kLog2e : INFINITY;
@@ -193,7 +215,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
         }
     };
     auto stage_publish = [&](LDS_AS float* lbuf, LDS_AS float* dbuf, float nl, float nd) __attribute__((always_inline)) {
-        if (wave == 0) {
+        if (wk == 0) {
             lbuf[lane] = nl;
             dbuf[lane] = nd;
         }
@@ -269,39 +291,74 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
             }
     };
 
-    auto step = [&](int s, auto par_tag) __attribute__((always_inline)) {
+    // Iteration i: this group's step s = GROUPS*i + grp (every group runs
+    // n_iter iterations, one barrier each; a group past its last step waits).
+    auto step = [&](int i, auto par_tag) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par_tag)::value;
+        const int s = GROUPS * i + grp;
         float nl = 0.f, nd = 0.f;
-        if (s + 1 < n_steps) stage_issue(s + 1, qL[1 - PAR], oL[1 - PAR], nl, nd);
-        const int hh = s / n_t;
-        const int t = t0 + (s - hh * n_t);
+        if (s + GROUPS < n_steps) stage_issue(s + GROUPS, qL[1 - PAR], oL[1 - PAR], nl, nd);
+        if (GROUPS == 1 || s < n_steps) {   // one group: s < n_steps always
+            const int hh = s / n_t;
+            const int t = t0 + (s - hh * n_t);
 #pragma unroll
-        for (int qb = 0; qb < kQStage / 32; ++qb) {
-            const int qs = t * kQStage + 32 * qb;
-            // Skip blocks past N, and (causal) blocks whose queries all precede
-            // this wave's keys.
-            if (qs < N && (!CAUSAL || qs + 31 >= kw)) block(qL[PAR], oL[PAR], lL[PAR], dL[PAR], qb, qs);
+            for (int qb = 0; qb < kQStage / 32; ++qb) {
+                const int qs = t * kQStage + 32 * qb;
+                // Skip blocks past N, and (causal) blocks whose queries all
+                // precede this wave's keys.
+                if (qs < N && (!CAUSAL || qs + 31 >= kw)) block(qL[PAR], oL[PAR], lL[PAR], dL[PAR], qb, qs);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the next stage's copies and loads
-        if (s + 1 < n_steps) stage_publish(lL[1 - PAR], dL[1 - PAR], nl, nd);
+        if (s + GROUPS < n_steps) stage_publish(lL[1 - PAR], dL[1 - PAR], nl, nd);
         __syncthreads();
     };
 
     {
         float nl = 0.f, nd = 0.f;
-        stage_issue(0, qL[0], oL[0], nl, nd);
+        if (grp < n_steps) stage_issue(grp, qL[0], oL[0], nl, nd);
         __builtin_amdgcn_s_waitcnt(0x0f70);
-        stage_publish(lL[0], dL[0], nl, nd);
+        if (grp < n_steps) stage_publish(lL[0], dL[0], nl, nd);
         __syncthreads();
     }
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    int s = 0;
-    for (; s + 1 < n_steps; s += 2) {
-        step(s, P0{});
-        step(s + 1, P1{});
+    int i = 0;
+    for (; i + 1 < n_iter; i += 2) {
+        step(i, P0{});
+        step(i + 1, P1{});
     }
-    if (s < n_steps) step(s, P0{});
+    if (i < n_iter) step(i, P0{});
+
+    if constexpr (GROUPS == 2) {
+        // Group 1 hands its partial sums to group 0 through the Q and dO
+        // tiles (no copy is in flight and every wave is past its last read):
+        // element j of the thread's 2*NDB*16 sums at float j*256 + 64 wk +
+        // lane, spread over the four tile arrays (a quarter each).
+        constexpr int kQuarter = GROUPS * T::kBytes / 4;   // floats per array
+        LDS_AS float* const red4[4] = {(LDS_AS float*)q_lds0, (LDS_AS float*)q_lds1,
+                                       (LDS_AS float*)o_lds0, (LDS_AS float*)o_lds1};
+        auto red = [&](int idx) -> LDS_AS float& { return red4[idx / kQuarter][idx % kQuarter]; };
+        const int slot = wk * 64 + lane;
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    red(((2 * db + 0) * 16 + r) * kBwdThreads + slot) = dk[db][r];
+                    red(((2 * db + 1) * 16 + r) * kBwdThreads + slot) = dv[db][r];
+                }
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dk[db][r] += red(((2 * db + 0) * 16 + r) * kBwdThreads + slot);
+                dv[db][r] += red(((2 * db + 1) * 16 + r) * kBwdThreads + slot);
+            }
+    }
 
     // dK = scale dK^T^T, dV = dV^T^T: lane l writes key `key`, entries
     // d = 32 db + 8 i4 + 4g .. +3.
@@ -503,8 +560,18 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_kt = (int)((p.N + kKeyBlock - 1) / kKeyBlock);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<IS_BF16, D, CAUSAL>), dim3((unsigned)(n_kt * p.BH_kv)),
-                       dim3(kBwdThreads), 0, s, p);
+    const dim3 grid_kv((unsigned)(n_kt * p.BH_kv));
+    bool split = false;
+    if constexpr (D == 64) {
+        if (p.G > 1) {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<IS_BF16, D, CAUSAL, 2>), grid_kv,
+                               dim3(2 * kBwdThreads), 0, s, p);
+            split = true;
+        }
+    }
+    if (!split)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<IS_BF16, D, CAUSAL, 1>), grid_kv, dim3(kBwdThreads), 0,
+                           s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_qt = (int)((p.N + kQueryBlock - 1) / kQueryBlock);
