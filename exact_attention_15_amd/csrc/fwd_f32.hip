@@ -8,8 +8,13 @@
 // (xf32) fp32 MFMA, so scores and P.V are exact fp32 products accumulated in
 // fp32 and P is never rounded below fp32.
 //
-// Layout: 4 wave64s x 32 query rows; K/V tiles of 32 keys. One lane owns
-// one query, as in the 16-bit kernel:
+// Layout: two groups of 4 wave64s x 32 query rows; K/V tiles of 32 keys.
+// Both groups own the same 128 query rows and take alternate K/V tiles (each
+// with its own LDS buffers), so the sequential length of a work item halves;
+// at the end group 1 hands its running (m, l, O) to group 0, which merges
+// them by the online-softmax rule (the rescale of "Flash Attention（二）
+// v2版本朴素实现 cuda core", section 1.3, applied across the two partial
+// results). One lane owns one query, as in the 16-bit kernel:
 //   S^T[key][query] = K . Q^T : the contraction over d is split so that lane
 //       half g takes d in [g*D/2, (g+1)*D/2): each lane reads D/2 contiguous
 //       floats of a K row (16-byte LDS reads) and keeps D/2 floats of Q.
@@ -30,13 +35,17 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kBlockN = 32;
-constexpr int kThreads = 256;
+constexpr int kGroupThreads = 256;   // a group: 4 waves x 32 query rows
+constexpr int kGroups = 2;           // groups per workgroup, alternate K/V tiles
+constexpr int kThreads = kGroupThreads * kGroups;
 
 template <int D>
 struct Smem32 {
     static constexpr int kRowBytes = D * 4;
     static constexpr int kTileBytes = kBlockN * D * 4;
-    static constexpr int kBytes = 4 * kTileBytes;   // K[2] + V[2]
+    static constexpr int kGroupBytes = 4 * kTileBytes;   // K[2] + V[2] of one group
+    static constexpr int kBytes = kGroups * kGroupBytes;
+    static_assert((D / 2 + 2) * kGroupThreads * 4 <= kBytes, "merge space");
 };
 
 // K rows: 16-byte chunk c of row r stored at chunk c ^ (r mod 8).
@@ -46,16 +55,18 @@ __device__ __forceinline__ int k_off32(int r, int c) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) void fwd32_kernel(FwdParams p) {
     using S = Smem32<D>;
-    constexpr int CH = D / 4;                          // 16-byte chunks per row
-    constexpr int ITEMS = kBlockN * CH / kThreads;     // chunks per thread per tensor
+    constexpr int CH = D / 4;                               // 16-byte chunks per row
+    constexpr int ITEMS = kBlockN * CH / kGroupThreads;     // chunks per thread per tensor
     constexpr int HALF = D / 2;
     static_assert(ITEMS >= 1, "tile / thread mismatch");
 
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ __attribute__((aligned(16))) char smem_all[S::kBytes];
 
-    const int tid = threadIdx.x;
+    const int grp = threadIdx.x / kGroupThreads;   // 0: even K/V tiles, 1: odd
+    const int tid = threadIdx.x % kGroupThreads;   // thread within the group
+    char* const smem = smem_all + grp * S::kGroupBytes;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int l32 = lane & 31;
@@ -94,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdParams p) {
     auto load_tile = [&](int kv0) {
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int item = tid + kThreads * it;
+            const int item = tid + kGroupThreads * it;
             const int r = item / CH, c = item % CH;
             const int key = kv0 + r;
             kreg[it] = key < N ? *(const f32x4*)(Kg + (size_t)key * D + 4 * c) : zero4;
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdParams p) {
         char* vs = smem + (2 + buf) * S::kTileBytes;
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int item = tid + kThreads * it;
+            const int item = tid + kGroupThreads * it;
             const int r = item / CH, c = item % CH;
             *(f32x4*)(ks + k_off32<D>(r, c)) = kreg[it];
             *(f32x4*)(vs + r * S::kRowBytes + 16 * c) = vreg[it];
@@ -122,16 +133,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
 
-    load_tile(0);
-    store_tile(0);
+    // Iteration it: this group's tile j = 2 it + grp. Both groups run n_iter
+    // iterations with one barrier each.
+    const int n_iter = (n_tiles + kGroups - 1) / kGroups;
+    if (grp < n_tiles) {
+        load_tile(grp * kBlockN);
+        store_tile(0);
+    }
     __syncthreads();
 
-    for (int j = 0; j < n_tiles; ++j) {
-        const int cur = j & 1;
+    for (int it = 0; it < n_iter; ++it) {
+        const int cur = it & 1;
+        const int j = kGroups * it + grp;
         const int kv0 = j * kBlockN;
-        if (j + 1 < n_tiles) load_tile(kv0 + kBlockN);
+        const bool next = j + kGroups < n_tiles;
+        if (next) load_tile(kv0 + kGroups * kBlockN);
 
-        const bool wave_live = !CAUSAL || kv0 <= q0 + wave * 32 + 31;
+        const bool wave_live = j < n_tiles && (!CAUSAL || kv0 <= q0 + wave * 32 + 31);
         if (wave_live) {
             const char* ks = smem + cur * S::kTileBytes;
             const float* vs = (const float*)(smem + (2 + cur) * S::kTileBytes);
@@ -193,8 +211,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdParams p) {
             }
         }
 
-        if (j + 1 < n_tiles) store_tile(cur ^ 1);
+        if (next) store_tile(cur ^ 1);
         __syncthreads();
+    }
+
+    // Merge: group 1's (m, l, O) through LDS (every tile read is done),
+    // value k of thread t at float k * 256 + t.
+    float* const mrg = (float*)smem_all;
+    if (grp == 1) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mrg[(db * 16 + i) * kGroupThreads + tid] = o[db][i];
+        mrg[(D / 2) * kGroupThreads + tid] = m_run;
+        mrg[(D / 2 + 1) * kGroupThreads + tid] = l_run;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    {
+        const float m1 = mrg[(D / 2) * kGroupThreads + tid];
+        const float l1 = mrg[(D / 2 + 1) * kGroupThreads + tid];
+        const float m = fmaxf(m_run, m1);
+        const float m_use = m == -INFINITY ? 0.f : m;
+        const float a0 = __builtin_amdgcn_exp2f(m_run - m_use);
+        const float a1 = __builtin_amdgcn_exp2f(m1 - m_use);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                o[db][i] = o[db][i] * a0 + mrg[(db * 16 + i) * kGroupThreads + tid] * a1;
+        l_run = l_run * a0 + l1 * a1;
+        m_run = m;
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -217,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd32_kernel(FwdParams p) {
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.n_qtiles * p.BH));
-    hipLaunchKernelGGL((fwd32_kernel<D, CAUSAL>), grid, dim3(kThreads), Smem32<D>::kBytes, s, p);
+    hipLaunchKernelGGL((fwd32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -1,0 +1,44 @@
+"""Host-side checks of bench.py's contract (no GPU): one GPU only, and the
+FLOP / byte accounting it reports."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_flop_and_byte_accounting():
+    # 4 B H N^2 d, halved for causal; the headline workload's figures
+    assert bench.attention_flops(4, 16, 4096, 64, True) == 137438953472
+    assert bench.attention_flops(1, 32, 8192, 128, False) == 1099511627776
+    assert bench.bwd_flops(4, 16, 4096, 64, True) == 2.5 * 137438953472
+    # Q, K, V, O once plus the fp32 lse; K and V with H_kv heads
+    assert bench.algorithmic_bytes(4, 16, 4096, 64, 2) == 135266304
+    assert bench.algorithmic_bytes(4, 16, 4096, 64, 2, H_kv=4) == \
+        2 * 4 * (16 + 4) * 4096 * 64 * 2 + 4 * 4 * 16 * 4096
+
+
+def test_traffic_is_tied_to_the_kernel_sources():
+    """roofline.traffic comes from committed counters only while the kernel
+    sources hash as they did when the counters were taken."""
+    import json
+    with open(bench.COUNTER_FILE) as f:
+        data = json.load(f)
+    entry = data["c3_bf16_causal"]
+    got = bench.measured_traffic("c3_bf16_causal")
+    if entry["kernel_source_sha"] == bench.kernel_source_hash():
+        assert got == entry["hbm_bytes_per_launch"]
+    else:
+        assert got is None
+    assert bench.measured_traffic("no_such_workload") is None
