@@ -222,6 +222,59 @@ def run_bwd(args, name, w):
     print(json.dumps(line), flush=True)
 
 
+def median_launch_ms(fn, n: int = 200) -> float:
+    """Median of n launches, each bracketed by its own pair of HIP events
+    (outside the timed region)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    for e0, e1 in pairs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
+    return ts[n // 2]
+
+
+def gfx_clock_under_load(fn, seconds: float = 0.3):
+    """Median GFX clock (MHz, from amdsmi) sampled while launches of fn keep
+    the GPU busy (outside the timed region); None where amdsmi is missing or
+    refuses."""
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
+    except Exception:
+        return None
+    clocks = []
+    try:
+        t_end = time.perf_counter() + seconds
+        for _ in range(20):   # queue work ahead of the first sample
+            fn()
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                fn()
+            info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            clk = info.get("clk") if isinstance(info, dict) else None
+            if isinstance(clk, (int, float)) and clk > 0:
+                clocks.append(float(clk))
+        torch.cuda.synchronize()
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+    if not clocks:
+        return None
+    clocks.sort()
+    return clocks[len(clocks) // 2]
+
+
 def _time_calls(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -402,6 +455,9 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(stop) / args.steps
+    step_fn = lambda: ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out)   # noqa: E731
+    ms_median = median_launch_ms(step_fn)
+    clock = gfx_clock_under_load(step_fn)
 
     flops = attention_flops(w.B, w.H, w.N, w.d, w.causal)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -430,6 +486,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": traffic},
+        "ms_median_launch": round(ms_median, 5),
+        "gfx_clock_mhz_under_load": clock,
         "algorithmic_gb_s": round(abytes / (ms * 1e-3) / 1e9, 1),
         "exp_per_s": (w.B * w.H * w.N * w.N / (2 if w.causal else 1)) / (ms * 1e-3),
         "parity_o_max_abs_sampled": parity,

@@ -55,8 +55,10 @@ def _check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what, n):
     err_l = np.abs(lse_gpu - lse_ref)
     assert np.all(np.isfinite(o_gpu)) and np.all(np.isfinite(lse_gpu)), what
     mo, ml = float(err_o.max()), float(err_l.max())
-    print(f"{what}: O max-abs {mo:.3e} mean-abs {float(err_o.mean()):.3e}; lse max-abs {ml:.3e}",
-          flush=True)
+    # noise-to-signal ratio ||O - O_ref|| / ||O_ref||
+    nsr = float(np.linalg.norm(o_gpu - o_ref) / max(np.linalg.norm(o_ref), 1e-300))
+    print(f"{what}: O max-abs {mo:.3e} mean-abs {float(err_o.mean()):.3e} NSR {nsr:.2e}; "
+          f"lse max-abs {ml:.3e}", flush=True)
     assert mo <= O_TOL[dtype], (what, mo)
     assert ml <= lse_tol(dtype, n), (what, ml)
 
