@@ -147,15 +147,20 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     LDS_AS float* const dL[2] = {(LDS_AS float*)d_lds0 + grp * kQStage,
                                  (LDS_AS float*)d_lds1 + grp * kQStage};
 
+    // Item w: key tile kt, K/V slice kv_bh, query-head split sp (of p.splits).
     const int w = blockIdx.x;
-    const int kt = w / p.BH_kv;
-    const int kv_bh = w - kt * p.BH_kv;
+    const int per_kt = p.BH_kv * p.splits;
+    const int kt = w / per_kt;
+    const int rem = w - kt * per_kt;
+    const int sp = rem / p.BH_kv;
+    const int kv_bh = rem - sp * p.BH_kv;
     const int k0 = kt * kKeyBlock;
     const int kw = k0 + 32 * wk;                 // first key of this wave
     const int key = kw + l32;                    // this lane's key
     const size_t kv_base = (size_t)kv_bh * (size_t)N * D;
-    // Query heads of this K/V head: bh0 .. bh0 + G - 1 (b*H + h_kv*G + g).
-    const int bh0 = kv_bh * p.G;
+    // This item's query heads: Gs of the K/V head's G (b*H + h_kv*G + sp*Gs + ...).
+    const int Gs = p.G / p.splits;
+    const int bh0 = kv_bh * p.G + sp * Gs;
 
     // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane l
     // holds row key, elements 16kd + 8g .. +7. Keys past N read as zero.
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     const int n_qt = (N + kQStage - 1) / kQStage;
     const int t0 = CAUSAL ? k0 / kQStage : 0;    // first query tile that sees these keys
     const int n_t = n_qt - t0;
-    const int n_steps = p.G * n_t;
+    const int n_steps = Gs * n_t;
     const int n_iter = (n_steps + GROUPS - 1) / GROUPS;   // steps GROUPS*i + grp
     const float c2 = p.scale_log2;
 
@@ -361,7 +366,28 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     }
 
     // dK = scale dK^T^T, dV = dV^T^T: lane l writes key `key`, entries
-    // d = 32 db + 8 i4 + 4g .. +3.
+    // d = 32 db + 8 i4 + 4g .. +3. With query-head splits the fp32 partial
+    // sums go to dq's memory instead ([split][dK, dV][B*H_kv][N][D], not yet
+    // scaled); bwd_kv_reduce_kernel adds them up before dq is written.
+    if (p.splits > 1) {
+        if (key < N) {
+            float* part = (float*)p.dq;
+            const size_t plane = (size_t)p.BH_kv * (size_t)N * D;
+            float* pk = part + (size_t)(2 * sp + 0) * plane + kv_base + (size_t)key * D;
+            float* pv = part + (size_t)(2 * sp + 1) * plane + kv_base + (size_t)key * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int dd = 32 * db + 8 * i4 + 4 * g;
+                    *(f32x4*)(pk + dd) = f32x4{dk[db][4 * i4], dk[db][4 * i4 + 1],
+                                               dk[db][4 * i4 + 2], dk[db][4 * i4 + 3]};
+                    *(f32x4*)(pv + dd) = f32x4{dv[db][4 * i4], dv[db][4 * i4 + 1],
+                                               dv[db][4 * i4 + 2], dv[db][4 * i4 + 3]};
+                }
+        }
+        return;
+    }
     if (key < N) {
         uint16_t* dkr = (uint16_t*)p.dk + kv_base + (size_t)key * D;
         uint16_t* dvr = (uint16_t*)p.dv + kv_base + (size_t)key * D;
@@ -379,6 +405,31 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
                 *(u32x2*)(dvr + dd) = vv;
             }
     }
+}
+
+// ---------------------------------------------------------------------------
+// (2b) With query-head splits: dK = scale * sum of the splits' partial dK^T,
+// dV = sum of the partial dV^T, in split order (deterministic); 4 elements
+// per thread.
+template <bool IS_BF16>
+__global__ __launch_bounds__(kBwdThreads) void bwd_kv_reduce_kernel(BwdParams p, int64_t plane) {
+    using Op = Op16<IS_BF16>;
+    const int64_t e4 = ((int64_t)blockIdx.x * kBwdThreads + threadIdx.x) * 4;
+    if (e4 >= plane) return;
+    const float* part = (const float*)p.dq;
+    f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < p.splits; ++sp) {
+        const f32x4 a = *(const f32x4*)(part + (2 * sp + 0) * plane + e4);
+        const f32x4 b = *(const f32x4*)(part + (2 * sp + 1) * plane + e4);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            sk[x] += a[x];
+            sv[x] += b[x];
+        }
+    }
+    const float sc = p.scale;
+    *(u32x2*)((uint16_t*)p.dk + e4) = u32x2{Op::pack2(sk[0] * sc, sk[1] * sc), Op::pack2(sk[2] * sc, sk[3] * sc)};
+    *(u32x2*)((uint16_t*)p.dv + e4) = u32x2{Op::pack2(sv[0], sv[1]), Op::pack2(sv[2], sv[3])};
 }
 
 // ---------------------------------------------------------------------------
@@ -560,23 +611,41 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_kt = (int)((p.N + kKeyBlock - 1) / kKeyBlock);
-    const dim3 grid_kv((unsigned)(n_kt * p.BH_kv));
-    bool split = false;
+    // Many query heads per K/V head leave few dK/dV items, each long: split
+    // the heads over up to G/4 items (a power of two dividing G) until there
+    // are ~512 items. The fp32 partial sums of S splits take 8 S B*H_kv*N*D
+    // bytes, which fit dq's 2 G B*H_kv*N*D bytes while S <= G/4; dq is
+    // written last.
+    BwdParams q = p;
+    q.splits = 1;
+    while (q.splits * 2 <= q.G / 4 && q.G % (q.splits * 2) == 0 &&
+           (int64_t)n_kt * q.BH_kv * q.splits < 512)
+        q.splits *= 2;
+    const dim3 grid_kv((unsigned)(n_kt * q.BH_kv * q.splits));
+    bool two_groups = false;
     if constexpr (D == 64) {
-        if (p.G > 1) {
+        if (q.G / q.splits > 1) {
             hipLaunchKernelGGL((bwd_dkdv_kernel<IS_BF16, D, CAUSAL, 2>), grid_kv,
-                               dim3(2 * kBwdThreads), 0, s, p);
-            split = true;
+                               dim3(2 * kBwdThreads), 0, s, q);
+            two_groups = true;
         }
     }
-    if (!split)
+    if (!two_groups)
         hipLaunchKernelGGL((bwd_dkdv_kernel<IS_BF16, D, CAUSAL, 1>), grid_kv, dim3(kBwdThreads), 0,
-                           s, p);
+                           s, q);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (q.splits > 1) {
+        const int64_t plane = (int64_t)q.BH_kv * q.N * D;
+        hipLaunchKernelGGL((bwd_kv_reduce_kernel<IS_BF16>),
+                           dim3((unsigned)((plane / 4 + kBwdThreads - 1) / kBwdThreads)),
+                           dim3(kBwdThreads), 0, s, q, plane);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int n_qt = (int)((p.N + kQueryBlock - 1) / kQueryBlock);
-    hipLaunchKernelGGL((bwd_dq_kernel<IS_BF16, D, CAUSAL>), dim3((unsigned)(n_qt * p.BH)),
-                       dim3(kBwdThreads), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<IS_BF16, D, CAUSAL>), dim3((unsigned)(n_qt * q.BH)),
+                       dim3(kBwdThreads), 0, s, q);
     return hipGetLastError();
 }
 

@@ -114,7 +114,10 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* ls
  *              the forward inputs, its output o and the incoming gradient.
  * k, v         DEVICE pointers, [B,H_kv,N,d] contiguous, `dtype`, 16-byte aligned.
  * lse          DEVICE pointer, [B,H,N] fp32: the forward's log-sum-exp.
- * dq           DEVICE pointer, [B,H,N,d] `dtype`, 16-byte aligned; written.
+ * dq           DEVICE pointer, [B,H,N,d] `dtype`, 16-byte aligned; written. With
+ *              8 or more query heads per K/V head its memory first holds the
+ *              fp32 partial sums of dk and dv (before dq itself is written),
+ *              so that the call allocates nothing.
  * dk, dv       DEVICE pointers, [B,H_kv,N,d] `dtype`, 16-byte aligned; written
  *              (not accumulated into).
  * delta        DEVICE pointer, [B,H,N] fp32, 4-byte aligned; written with D_i

@@ -68,7 +68,10 @@ def _bwd_and_check(ea, oracle_lib, q, k, v, dout, causal, scale, what):
 
 
 SWEEP = [(1, 2, 2), (2, 4, 1), (17, 2, 2), (64, 4, 2), (65, 2, 2), (127, 6, 3), (128, 2, 2),
-         (129, 4, 4), (200, 4, 1), (257, 2, 2)]
+         (129, 4, 4), (200, 4, 1), (257, 2, 2),
+         # 8 or 16 query heads per K/V head: the dK/dV work is split over
+         # query-head groups whose partial sums are reduced afterwards
+         (65, 16, 1), (130, 8, 1), (257, 16, 2)]
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
@@ -83,6 +86,16 @@ def test_bwd_sweep_small(ea, oracle_lib, dtype, d, causal):
         dout = make_dout(2, H, n, d, dtype, seed=seed)
         _bwd_and_check(ea, oracle_lib, q, k, v, dout, causal, ea.default_scale(d),
                        f"N={n} H={H} H_kv={H_kv} d={d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_mqa_midsize(ea, oracle_lib, d):
+    """Multi-query attention (16 query heads, one K/V head) at N = 2048,
+    causal: the split dK/dV path with four query-head groups, every element."""
+    q, k, v = make_qkv(1, 16, 2048, d, torch.bfloat16, seed=9800 + d, H_kv=1)
+    dout = make_dout(1, 16, 2048, d, torch.bfloat16, seed=9800 + d)
+    _bwd_and_check(ea, oracle_lib, q, k, v, dout, True, ea.default_scale(d),
+                   f"MQA H=16 N=2048 d={d}")
 
 
 def test_bwd_scale_and_values(ea, oracle_lib):
