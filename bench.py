@@ -135,9 +135,6 @@ def run_bwd(args, name, w):
     from exact_attention_15_amd.inputs import workload_dout, workload_inputs
 
     dt_name = DTYPE_NAME[str(w.dtype)]
-    if dt_name == "fp32":
-        print("bench.py: the backward pass takes fp16 / bf16 inputs", file=sys.stderr)
-        sys.exit(2)
     ea.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -161,8 +158,8 @@ def run_bwd(args, name, w):
         grads = ea.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, out=out)
         torch.cuda.synchronize()
         ref = oracle.attn_bwd_ref(*sub, w.causal, w.scale, error_scales=True)
-        u = 2.0 ** -8 if dt_name == "bf16" else 2.0 ** -11
-        s_half = 2.0 ** -134 if dt_name == "bf16" else 2.0 ** -25
+        u = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11, "fp32": 2.0 ** -12}[dt_name]
+        s_half = {"bf16": 2.0 ** -134, "fp16": 2.0 ** -25, "fp32": 2.0 ** -150}[dt_name]
         worst = 0.0
         for got, r, e, z in zip((grads[0][:1, :G], grads[1][:1, :1], grads[2][:1, :1]),
                                 ref[:3], ref[3:6], ref[6:9]):

@@ -148,7 +148,7 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     ``dout`` of ``o``, from the forward's ``o`` and ``lse``.
 
     q, o, dout: [B,H,N,d]; k, v: [B,H_kv,N,d]; lse: float32 [B,H,N]; all on
-    one GPU, contiguous, q/k/v/o/dout of one 16-bit dtype. ``out`` may pass
+    one GPU, contiguous, q/k/v/o/dout of one dtype. ``out`` may pass
     preallocated ``(dq, dk, dv, delta)`` (delta: float32 [B,H,N], written
     with the row statistic D_i = dout_i . o_i).
     """

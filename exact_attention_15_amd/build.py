@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["attn_api.hip", "fwd_mfma16.hip", "fwd_f32.hip", "bwd_mfma16.hip", "unfused.hip"]
+SOURCES = ["attn_api.hip", "fwd_mfma16.hip", "fwd_f32.hip", "bwd_mfma16.hip", "bwd_f32.hip",
+           "unfused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -74,7 +74,6 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     if (!dout || !dq || !dk || !dv || !delta) return ATTN_EINVAL;
     // The row-statistic kernel covers 16 rows or more per workgroup.
     if (B * H * N / 16 >= (int64_t)INT32_MAX) return ATTN_EINVAL;
-    if (dtype == ATTN_F32) return ATTN_EUNSUPPORTED;
     const uintptr_t mis = ((uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u;
     if (mis != 0 || ((uintptr_t)delta & 3u) != 0) return ATTN_EALIGN;
 
@@ -99,8 +98,10 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 
     (void)hipGetLastError();
-    const hipError_t e = attn::launch_bwd16(p, dtype == ATTN_BF16, (int)d, causal != 0,
-                                            (hipStream_t)stream);
+    const hipError_t e =
+        dtype == ATTN_F32
+            ? attn::launch_bwd32(p, (int)d, causal != 0, (hipStream_t)stream)
+            : attn::launch_bwd16(p, dtype == ATTN_BF16, (int)d, causal != 0, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
@@ -153,7 +154,7 @@ extern "C" const char* attn_strerror(int code) {
     switch (code) {
         case ATTN_OK: return "ok";
         case ATTN_EINVAL: return "invalid argument (pointer, size, H_kv, dtype, scale or causal)";
-        case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128), or fp32 in attn_bwd / attn_fwd_unfused";
+        case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128), or fp32 in attn_fwd_unfused";
         case ATTN_EALIGN: return "a tensor pointer is misaligned (16 bytes; lse, delta 4; workspace 256)";
         case ATTN_EHIP: return "HIP kernel launch failed";
         default: return "unknown error code";

@@ -39,7 +39,7 @@ typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
 enum {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,       /* bad argument (null pointer, size, H_kv, dtype, scale, causal) */
-    ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128; fp32 in attn_bwd or
+    ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128; fp32 in
                                attn_fwd_unfused */
     ATTN_EALIGN = -3,       /* a base pointer misaligned (see each function) */
     ATTN_EHIP = -4          /* the HIP launch failed */
@@ -114,10 +114,10 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* ls
  *              the forward inputs, its output o and the incoming gradient.
  * k, v         DEVICE pointers, [B,H_kv,N,d] contiguous, `dtype`, 16-byte aligned.
  * lse          DEVICE pointer, [B,H,N] fp32: the forward's log-sum-exp.
- * dq           DEVICE pointer, [B,H,N,d] `dtype`, 16-byte aligned; written. With
- *              8 or more query heads per K/V head its memory first holds the
- *              fp32 partial sums of dk and dv (before dq itself is written),
- *              so that the call allocates nothing.
+ * dq           DEVICE pointer, [B,H,N,d] `dtype`, 16-byte aligned; written. For
+ *              f16/bf16 with 8 or more query heads per K/V head its memory
+ *              first holds the fp32 partial sums of dk and dv (before dq
+ *              itself is written), so that the call allocates nothing.
  * dk, dv       DEVICE pointers, [B,H_kv,N,d] `dtype`, 16-byte aligned; written
  *              (not accumulated into).
  * delta        DEVICE pointer, [B,H,N] fp32, 4-byte aligned; written with D_i
@@ -126,10 +126,10 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* ls
  *              allocates nothing; its contents are valid after the call.
  * B, H, H_kv, N, d, causal, scale
  *              as for attn_fwd_gqa.
- * dtype        ATTN_F16 or ATTN_BF16 (fp32: ATTN_EUNSUPPORTED). Products are
- *              accumulated in fp32; p and ds are rounded to `dtype` as the
- *              operands of the dv, dk and dq products; outputs are rounded
- *              once (nearest even) from fp32.
+ * dtype        ATTN_F32, ATTN_F16 or ATTN_BF16. Products are accumulated in
+ *              fp32; for f16/bf16, p and ds are rounded to `dtype` as the
+ *              operands of the dv, dk and dq products and outputs are rounded
+ *              once (nearest even) from fp32; fp32 rounds nothing below fp32.
  * stream       hipStream_t (NULL = the null stream).
  *
  * Asynchronous: three kernels are enqueued on `stream` and the call returns;

@@ -151,7 +151,6 @@ def test_bwd_argument_validation(attn_lib_path):
         (dict(scale=float("nan")), ea.ATTN_EINVAL),
         (dict(dtype=5), ea.ATTN_EINVAL),
         (dict(d=96), ea.ATTN_EUNSUPPORTED),
-        (dict(dtype=ea.ATTN_F32), ea.ATTN_EUNSUPPORTED),
         (dict(dout=P + 0x5008), ea.ATTN_EALIGN),
         (dict(dq=P + 0x6004), ea.ATTN_EALIGN),
         (dict(dk=P + 0x7002), ea.ATTN_EALIGN),

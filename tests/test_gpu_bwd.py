@@ -8,7 +8,9 @@ from the error analysis of that arithmetic (first order):
     |g - g_ref| <= 2 [(u + n_acc 2^-24) (e + |g_ref|) + (s/2) (z + 1)]
 Rounding x to the 16-bit type errs by at most u|x| + s/2: u its unit
 roundoff (2^-8 bf16, 2^-11 fp16), s its subnormal spacing (2^-24 fp16,
-2^-133 bf16). p and ds are rounded to it as matrix-core operands, o was
+2^-133 bf16); fp32 rounds nothing below fp32 (u = 0). To u is added the
+relative error of p from the fp32 scores, |ds| <= d 2^-24 scale
+max_ij sum_c |q_ic k_jc| (computed from the inputs), and 2^-22 for exp2. p and ds are rounded to it as matrix-core operands, o was
 rounded to it, and the output is rounded to it; e and z are the oracle's
 error scales of the element (the sums of the magnitudes those roundings
 perturb, relatively and absolutely); n_acc = G N / 16 + 32 bounds the fp32
@@ -26,8 +28,8 @@ from exact_attention_15_amd.inputs import WORKLOADS, make_dout, make_qkv, worklo
 
 pytestmark = pytest.mark.gpu
 
-U = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
-SUB = {torch.float16: 2.0 ** -24, torch.bfloat16: 2.0 ** -133}
+U = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8, torch.float32: 0.0}
+SUB = {torch.float16: 2.0 ** -24, torch.bfloat16: 2.0 ** -133, torch.float32: 2.0 ** -149}
 
 
 @pytest.fixture(scope="module")
@@ -44,10 +46,20 @@ def _fwd_stats(oracle_lib, q, k, v, causal, scale):
     return torch.from_numpy(o_ref).to(q.dtype), torch.from_numpy(lse_ref).to(torch.float32)
 
 
-def _check(got, ref, err, zerr, dtype, n_acc, what):
+def _score_term(q, k, scale):
+    """d 2^-24 scale max_ij sum_c |q_ic k_jc| + 2^-22: the relative error of p
+    that the fp32 scores and exp2 can cause."""
+    G = q.shape[1] // k.shape[1]
+    qa = q.to(torch.float64).abs()
+    ka = k.to(torch.float64).abs().repeat_interleave(G, dim=1)
+    m = float(torch.matmul(qa, ka.transpose(-1, -2)).max())
+    return q.shape[-1] * 2.0 ** -24 * float(scale) * m + 2.0 ** -22
+
+
+def _check(got, ref, err, zerr, dtype, n_acc, what, u_s):
     got = got.to(torch.float64).cpu().numpy() if isinstance(got, torch.Tensor) else got
     assert np.all(np.isfinite(got)), what
-    bound = 2 * ((U[dtype] + n_acc * 2.0 ** -24) * (err + np.abs(ref)) +
+    bound = 2 * ((U[dtype] + u_s + n_acc * 2.0 ** -24) * (err + np.abs(ref)) +
                  SUB[dtype] / 2 * (zerr + 1))
     diff = np.abs(got - ref)
     ratio = float((diff / np.maximum(bound, 1e-300)).max())
@@ -62,9 +74,10 @@ def _bwd_and_check(ea, oracle_lib, q, k, v, dout, causal, scale, what):
     rq, rk, rv, eq, ek, ev, zq, zk, zv = oracle_lib.attn_bwd_ref(q, k, v, dout, causal, scale,
                                                                  error_scales=True)
     n_acc = (q.shape[1] // k.shape[1]) * q.shape[2] / 16 + 32
-    _check(dq, rq, eq, zq, q.dtype, n_acc, what + " dq")
-    _check(dk, rk, ek, zk, q.dtype, n_acc, what + " dk")
-    _check(dv, rv, ev, zv, q.dtype, n_acc, what + " dv")
+    u_s = _score_term(q, k, scale)
+    _check(dq, rq, eq, zq, q.dtype, n_acc, what + " dq", u_s)
+    _check(dk, rk, ek, zk, q.dtype, n_acc, what + " dk", u_s)
+    _check(dv, rv, ev, zv, q.dtype, n_acc, what + " dv", u_s)
 
 
 SWEEP = [(1, 2, 2), (2, 4, 1), (17, 2, 2), (64, 4, 2), (65, 2, 2), (127, 6, 3), (128, 2, 2),
@@ -74,7 +87,8 @@ SWEEP = [(1, 2, 2), (2, 4, 1), (17, 2, 2), (64, 4, 2), (65, 2, 2), (127, 6, 3), 
          (65, 16, 1), (130, 8, 1), (257, 16, 2)]
 
 
-@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32],
+                         ids=["f16", "bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_bwd_sweep_small(ea, oracle_lib, dtype, d, causal):
@@ -105,7 +119,7 @@ def test_bwd_scale_and_values(ea, oracle_lib):
     _bwd_and_check(ea, oracle_lib, q, k, v, dout, True, 0.3, "scale 0.3, values x2")
 
 
-FULL = ["c3_bf16_causal", "g1_bf16_causal_gqa4", "c4_bf16_d128_causal"]
+FULL = ["c3_bf16_causal", "g1_bf16_causal_gqa4", "c4_bf16_d128_causal", "c2_f32_causal"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -141,9 +155,10 @@ def test_bwd_workload_full_size(ea, oracle_lib, name):
                                                                      error_scales=True)
         hs = slice(hk * G, (hk + 1) * G)
         tag = f"{name} slice b={b} h_kv={hk}"
-        _check(dq[b:b + 1, hs], rq, eq, zq, w.dtype, n_acc, tag + " dq")
-        _check(dk[b:b + 1, hk:hk + 1], rk, ek, zk, w.dtype, n_acc, tag + " dk")
-        _check(dv[b:b + 1, hk:hk + 1], rv, ev, zv, w.dtype, n_acc, tag + " dv")
+        u_s = _score_term(sub[0], sub[1], w.scale)
+        _check(dq[b:b + 1, hs], rq, eq, zq, w.dtype, n_acc, tag + " dq", u_s)
+        _check(dk[b:b + 1, hk:hk + 1], rk, ek, zk, w.dtype, n_acc, tag + " dk", u_s)
+        _check(dv[b:b + 1, hk:hk + 1], rv, ev, zv, w.dtype, n_acc, tag + " dv", u_s)
     # Identities on every slice: the keys' gradients sum to zero over keys;
     # the values' gradients sum to the group's summed dout.
     dk64 = dk.to(torch.float64)
