@@ -50,7 +50,7 @@ def load_library():
     lib.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                      ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.attn_fwd_unfused.restype = ctypes.c_int
-    lib.attn_unfused_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.attn_unfused_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
     lib.attn_unfused_workspace_bytes.restype = i64
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -205,15 +205,16 @@ def attn_fwd_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, ca
                                            d, int(causal), float(scale), int(dtype), stream)
 
 
-def unfused_workspace_bytes(B: int, H: int, N: int) -> int:
-    return int(load_library().attn_unfused_workspace_bytes(B, H, N))
+def unfused_workspace_bytes(B: int, H: int, N: int, dtype: int) -> int:
+    """Workspace bytes of ``attn_fwd_unfused`` for the dtype code ``dtype``."""
+    return int(load_library().attn_unfused_workspace_bytes(B, H, N, int(dtype)))
 
 
 def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, workspace=None):
     """The unfused forward (S, softmax, P V as three kernels with N x N
     buffers): the comparison path. Returns (o, lse) like ``fwd``.
     ``workspace`` may pass a preallocated uint8 device tensor of at least
-    ``unfused_workspace_bytes(B, H, N)`` bytes."""
+    ``unfused_workspace_bytes(B, H, N, dtype_code(q.dtype))`` bytes."""
     import torch
     if not (q.shape == k.shape == v.shape) or q.dim() != 4:
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
@@ -225,7 +226,7 @@ def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, works
     B, H, N, d = q.shape
     if scale is None:
         scale = default_scale(d)
-    need = unfused_workspace_bytes(B, H, N)
+    need = unfused_workspace_bytes(B, H, N, dtype_code(q.dtype))
     if need < 0:
         raise ValueError("sizes out of range")
     if workspace is None:

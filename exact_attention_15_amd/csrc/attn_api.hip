@@ -105,11 +105,13 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
-extern "C" int64_t attn_unfused_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+extern "C" int64_t attn_unfused_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype) {
     if (B < 1 || H < 1 || N < 1 || N > (int64_t)INT32_MAX - 64) return -1;
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return -1;
     const int64_t ld = (N + 63) / 64 * 64;
     if (B > INT64_MAX / H || B * H > INT64_MAX / N || B * H * N > INT64_MAX / ld / 8) return -1;
-    return B * H * N * ld * 6;   // fp32 scores + 16-bit probabilities
+    // fp32 scores + probabilities in the input type
+    return B * H * N * ld * (dtype == ATTN_F32 ? 8 : 6);
 }
 
 extern "C" int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -119,11 +121,10 @@ extern "C" int attn_fwd_unfused(const void* q, const void* k, const void* v, voi
     const int rc = validate(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype);
     if (rc != ATTN_OK) return rc;
     if (!workspace) return ATTN_EINVAL;
-    const int64_t need = attn_unfused_workspace_bytes(B, H, N);
+    const int64_t need = attn_unfused_workspace_bytes(B, H, N, dtype);
     if (need < 0 || workspace_bytes < need) return ATTN_EINVAL;
     const int64_t nt = (N + 63) / 64;
     if (B * H > (int64_t)INT32_MAX / nt / nt) return ATTN_EINVAL;   // one-dimensional grid
-    if (dtype == ATTN_F32) return ATTN_EUNSUPPORTED;
     if (((uintptr_t)workspace & 255u) != 0) return ATTN_EALIGN;
 
     attn::UnfusedParams p;
@@ -140,7 +141,10 @@ extern "C" int attn_fwd_unfused(const void* q, const void* k, const void* v, voi
     p.s = (float*)workspace;
     p.pm = (char*)workspace + B * H * N * p.ld * 4;
     (void)hipGetLastError();
-    const hipError_t e = attn::launch_unfused16(p, dtype == ATTN_BF16, (int)d, (hipStream_t)stream);
+    const hipError_t e =
+        dtype == ATTN_F32
+            ? attn::launch_unfused32(p, (int)d, (hipStream_t)stream)
+            : attn::launch_unfused16(p, dtype == ATTN_BF16, (int)d, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
@@ -154,7 +158,7 @@ extern "C" const char* attn_strerror(int code) {
     switch (code) {
         case ATTN_OK: return "ok";
         case ATTN_EINVAL: return "invalid argument (pointer, size, H_kv, dtype, scale or causal)";
-        case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128), or fp32 in attn_fwd_unfused";
+        case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128)";
         case ATTN_EALIGN: return "a tensor pointer is misaligned (16 bytes; lse, delta 4; workspace 256)";
         case ATTN_EHIP: return "HIP kernel launch failed";
         default: return "unknown error code";

@@ -88,5 +88,6 @@ hipError_t launch_fwd32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd16(const BwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd32(const BwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_unfused16(const UnfusedParams& p, bool is_bf16, int d, hipStream_t s);
+hipError_t launch_unfused32(const UnfusedParams& p, int d, hipStream_t s);
 
 }  // namespace attn

@@ -39,8 +39,7 @@ typedef enum { ATTN_F32 = 0, ATTN_F16 = 1, ATTN_BF16 = 2 } attn_dtype_t;
 enum {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,       /* bad argument (null pointer, size, H_kv, dtype, scale, causal) */
-    ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128; fp32 in
-                               attn_fwd_unfused */
+    ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128 */
     ATTN_EALIGN = -3,       /* a base pointer misaligned (see each function) */
     ATTN_EHIP = -4          /* the HIP launch failed */
 };
@@ -152,9 +151,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * probability 0.
  *
  * q, k, v, o, lse, B, H, N, d, causal, scale, stream: as for attn_fwd.
- * dtype        ATTN_F16 or ATTN_BF16 (fp32: ATTN_EUNSUPPORTED).
+ * dtype        ATTN_F32, ATTN_F16 or ATTN_BF16.
  * workspace    DEVICE pointer, 256-byte aligned, of workspace_bytes >=
- *              attn_unfused_workspace_bytes(B, H, N) bytes, owned by the
+ *              attn_unfused_workspace_bytes(B, H, N, dtype) bytes, owned by the
  *              caller; overwritten (S and P, rows padded to a multiple of 64
  *              columns). Too small or NULL: ATTN_EINVAL.
  * Asynchronous on `stream`, allocates nothing; validation precedes any HIP
@@ -164,9 +163,11 @@ int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, float
                      void* workspace, int64_t workspace_bytes, int64_t B, int64_t H, int64_t N,
                      int64_t d, int causal, float scale, int dtype, void* stream);
 
-/* attn_unfused_workspace_bytes — bytes of workspace attn_fwd_unfused needs:
- * B*H*N*ld*6 with ld = N rounded up to 64; -1 for sizes out of range. */
-int64_t attn_unfused_workspace_bytes(int64_t B, int64_t H, int64_t N);
+/* attn_unfused_workspace_bytes — bytes of workspace attn_fwd_unfused needs
+ * for `dtype`: B*H*N*ld*(4 + p) with ld = N rounded up to 64 and p the bytes
+ * of one probability (4 for ATTN_F32, 2 for ATTN_F16 / ATTN_BF16); -1 for
+ * sizes out of range or an unknown dtype. */
+int64_t attn_unfused_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype);
 
 /* attn_strerror — static description of a return code (never NULL). */
 const char* attn_strerror(int code);

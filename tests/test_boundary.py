@@ -167,13 +167,17 @@ def test_bwd_argument_validation(attn_lib_path):
 
 def test_unfused_workspace_and_validation(attn_lib_path):
     import exact_attention_15_amd as ea
-    assert ea.unfused_workspace_bytes(1, 1, 1) == 64 * 6
-    assert ea.unfused_workspace_bytes(2, 3, 100) == 2 * 3 * 100 * 128 * 6
-    assert ea.unfused_workspace_bytes(4, 16, 4096) == 4 * 16 * 4096 * 4096 * 6
-    for bad in [(0, 1, 1), (1, -1, 4), (1, 1, 0)]:
+    BF, F16, F32 = ea.ATTN_BF16, ea.ATTN_F16, ea.ATTN_F32
+    assert ea.unfused_workspace_bytes(1, 1, 1, BF) == 64 * 6
+    assert ea.unfused_workspace_bytes(2, 3, 100, F16) == 2 * 3 * 100 * 128 * 6
+    assert ea.unfused_workspace_bytes(4, 16, 4096, BF) == 4 * 16 * 4096 * 4096 * 6
+    # fp32 keeps the probabilities in fp32: 4 + 4 bytes per score.
+    assert ea.unfused_workspace_bytes(1, 1, 1, F32) == 64 * 8
+    assert ea.unfused_workspace_bytes(2, 3, 100, F32) == 2 * 3 * 100 * 128 * 8
+    for bad in [(0, 1, 1, BF), (1, -1, 4, BF), (1, 1, 0, F32), (1, 1, 4, 7)]:
         assert ea.unfused_workspace_bytes(*bad) == -1
     P = 0x7f0000000000
-    need = ea.unfused_workspace_bytes(1, 2, 128)
+    need = ea.unfused_workspace_bytes(1, 2, 128, BF)
     good = dict(q=P, k=P + 0x1000, v=P + 0x2000, o=P + 0x3000, lse=P + 0x4000,
                 ws=P + 0x10000, wsb=need, B=1, H=2, N=128, d=64, causal=1, scale=0.125,
                 dtype=ea.ATTN_BF16, stream=None)
@@ -183,7 +187,10 @@ def test_unfused_workspace_and_validation(attn_lib_path):
         (dict(q=None), ea.ATTN_EINVAL),
         (dict(N=0), ea.ATTN_EINVAL),
         (dict(causal=3), ea.ATTN_EINVAL),
-        (dict(dtype=ea.ATTN_F32), ea.ATTN_EUNSUPPORTED),
+        (dict(dtype=ea.ATTN_F32), ea.ATTN_EINVAL),   # fp32 needs 8 bytes per score
+        (dict(dtype=ea.ATTN_F32, wsb=ea.unfused_workspace_bytes(1, 2, 128, F32),
+              d=96), ea.ATTN_EUNSUPPORTED),
+        (dict(dtype=9), ea.ATTN_EINVAL),
         (dict(d=32), ea.ATTN_EUNSUPPORTED),
         (dict(ws=P + 0x10080), ea.ATTN_EALIGN),
         (dict(o=P + 0x3008), ea.ATTN_EALIGN),
