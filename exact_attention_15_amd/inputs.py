@@ -110,3 +110,39 @@ def workload_dout(w: Workload):
 
 def workload_inputs(w: Workload):
     return make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.value_scale, w.H_kv)
+
+
+def make_structured_qkv(kind: str, B: int, H: int, N: int, d: int, dtype: torch.dtype,
+                        seed: int, peak: float = 40.0):
+    """Inputs whose score rows have a chosen shape, to drive the online
+    softmax's running maximum (drawn in float32, then rounded to the dtype):
+
+    * ``"rising"``:  q_i = u + 0.25 n, k_j = (peak j / N) u / sqrt(d) + 0.25 n
+      with u a random +-1 vector and n fresh N(0,1) noise, so that (at the
+      default scale 1/sqrt(d)) the score of key j grows by about peak / N per
+      key: the row maximum moves on every key tile.
+    * ``"falling"``: the same with j replaced by N - 1 - j: the maximum sits
+      in the first tile and never moves afterwards.
+    * ``"wide"``:    Q, K i.i.d. N(0, 4), scores with standard deviation ~4:
+      rows are nearly one-hot and their maxima jump irregularly.
+
+    V is i.i.d. N(0,1) in every case.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    if kind == "wide":
+        q = torch.randn((B, H, N, d), dtype=torch.float32, generator=g) * 2.0
+        k = torch.randn((B, H, N, d), dtype=torch.float32, generator=g) * 2.0
+    elif kind in ("rising", "falling"):
+        u = torch.randint(0, 2, (B, H, 1, d), generator=g).to(torch.float32) * 2.0 - 1.0
+        q = u + 0.25 * torch.randn((B, H, N, d), dtype=torch.float32, generator=g)
+        j = torch.arange(N, dtype=torch.float32)
+        if kind == "falling":
+            j = (N - 1) - j
+        ramp = (peak / N) * j / (d ** 0.5)
+        k = ramp.view(1, 1, N, 1) * u + 0.25 * torch.randn((B, H, N, d), dtype=torch.float32,
+                                                            generator=g)
+    else:
+        raise ValueError(f"unknown kind {kind!r}")
+    v = torch.randn((B, H, N, d), dtype=torch.float32, generator=g)
+    return tuple(x.to(dtype).contiguous() for x in (q, k, v))

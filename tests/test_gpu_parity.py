@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_15_amd.inputs import WORKLOADS, make_qkv, workload_inputs
+from exact_attention_15_amd.inputs import WORKLOADS, make_qkv, make_structured_qkv, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -173,6 +173,44 @@ def test_invariants_on_gpu(ea, dtype, causal):
     assert np.abs(p.sum(1) - 1).max() <= 2 * tol
     if causal:
         assert np.all(p[np.triu_indices(n, 1)] == 0.0)
+
+
+def _score_term(q, k, scale):
+    """lse error allowance for the fp32 scores, in nats: the kernel's score
+    is an fp32 sum of d products, then one fma with the fp32 constant
+    scale*log2(e) and one exp2, so its error is at most about
+    scale (d + 2) 2^-24 max_ij sum_c |q_ic k_jc| (plus 2^-20 for the exp2
+    argument's own rounding); the lse moves by at most that much."""
+    qa = q.to(torch.float64).abs()
+    ka = k.to(torch.float64).abs()
+    m = float(torch.matmul(qa, ka.transpose(-1, -2)).max())
+    d = q.shape[-1]
+    return scale * (d + 2) * 2.0 ** -24 * m + 2.0 ** -20
+
+
+@pytest.mark.parametrize("kind", ["rising", "falling", "wide"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16],
+                         ids=["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_running_max_paths(ea, oracle_lib, kind, dtype, d, causal):
+    """Score rows shaped to drive the online softmax's running maximum:
+    rising rows move it by ~8 nats on every full 64-key tile (the accumulator
+    is rescaled on every tile), falling rows fix it in the first tile, wide
+    rows (score std ~4) make it jump irregularly. N = 300 spans five key
+    tiles with a ragged tail."""
+    n = 300
+    q, k, v = make_structured_qkv(kind, 1, 2, n, d, dtype, seed=4100 + d)
+    scale = ea.default_scale(d)
+    o, lse = _run_gpu(ea, q, k, v, causal, scale)
+    o_ref, lse_ref = oracle_lib.attn_fwd_ref(q, k, v, causal, scale)
+    err_o = float(np.abs(o - o_ref).max())
+    err_l = float(np.abs(lse - lse_ref).max())
+    tol_l = lse_tol(dtype, n) + _score_term(q, k, scale)
+    print(f"{kind} d={d} {dtype} causal={causal}: O max-abs {err_o:.3e}, lse max-abs "
+          f"{err_l:.3e} (bound {tol_l:.3e})", flush=True)
+    assert np.all(np.isfinite(o)) and err_o <= O_TOL[dtype], err_o
+    assert err_l <= tol_l, err_l
 
 
 def test_deterministic(ea):
