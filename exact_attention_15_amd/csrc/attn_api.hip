@@ -22,9 +22,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
     if (!isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_EINVAL;
     // Positions are 32-bit inside the kernels; the grid is one-dimensional.
-    if (N > (int64_t)INT32_MAX - attn::kBlockM) return ATTN_EINVAL;
+    if (N > (int64_t)INT32_MAX - attn::kMinBlockM) return ATTN_EINVAL;
     if (B > INT32_MAX / H) return ATTN_EINVAL;
-    const int64_t n_qtiles = (N + attn::kBlockM - 1) / attn::kBlockM;
+    const int64_t n_qtiles = (N + attn::kMinBlockM - 1) / attn::kMinBlockM;
     if (n_qtiles * B * H > (int64_t)INT32_MAX) return ATTN_EINVAL;
     if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
@@ -51,7 +51,7 @@ extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o
     p.BH_kv = (int)(B * H_kv);
     p.H_kv = (int)H_kv;
     p.G = (int)(H / H_kv);
-    p.n_qtiles = (int)((N + attn::kBlockM - 1) / attn::kBlockM);
+    p.n_qtiles = 0;   // set by the launcher for its own query tile
     // scale * log2(e), rounded once to fp32: scores go straight into exp2.
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 

@@ -79,8 +79,9 @@ struct UnfusedParams {
     float scale;
 };
 
-// Query rows per workgroup for every kernel here.
-constexpr int kBlockM = 128;
+// The fewest query rows any forward workgroup takes (fp32, d = 64); bounds
+// the one-dimensional grids.
+constexpr int kMinBlockM = 64;
 
 // Launchers return the hipError_t of the launch.
 hipError_t launch_fwd16(const FwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s);
