@@ -382,7 +382,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by (b,h) slices with no exchange, but no multi-GPU run exists)",
               file=sys.stderr)
         sys.exit(2)
