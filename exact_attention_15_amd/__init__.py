@@ -1,4 +1,4 @@
-"""Exact attention forward for MI355X (gfx950).
+"""Exact attention (forward, backward, unfused comparison) for MI355X (gfx950).
 
 Thin Python binding over the C ABI of ``libattn.so`` (``include/attn.h``):
 it checks tensors, allocates the outputs with torch on the inputs' device
@@ -22,9 +22,10 @@ _lib = None
 
 
 class AttnError(RuntimeError):
-    def __init__(self, code: int, msg: str):
-        super().__init__(f"attn_fwd failed ({code}): {msg}")
+    def __init__(self, code: int, msg: str, entry: str = "attn_fwd"):
+        super().__init__(f"{entry} failed ({code}): {msg}")
         self.code = code
+        self.entry = entry
 
 
 def load_library():
@@ -132,7 +133,7 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None):
                           lse.data_ptr(), B, H, H_kv, N, d, causal, scale,
                           dtype_code(q.dtype), stream)
     if rc != ATTN_OK:
-        raise AttnError(rc, strerror(rc))
+        raise AttnError(rc, strerror(rc), "attn_fwd_gqa")
     return o, lse
 
 
@@ -194,7 +195,7 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
                       delta.data_ptr(), B, H, H_kv, N, d, causal, scale,
                       dtype_code(q.dtype), stream)
     if rc != ATTN_OK:
-        raise AttnError(rc, strerror(rc))
+        raise AttnError(rc, strerror(rc), "attn_bwd")
     return dq, dk, dv
 
 
@@ -239,7 +240,7 @@ def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, works
                               lse.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N,
                               d, causal, scale, dtype_code(q.dtype), stream)
     if rc != ATTN_OK:
-        raise AttnError(rc, strerror(rc))
+        raise AttnError(rc, strerror(rc), "attn_fwd_unfused")
     return o, lse
 
 
