@@ -171,10 +171,12 @@ def test_bwd_workload_full_size(ea, oracle_lib, name):
     assert torch.all(dk64.sum(dim=2).abs() <= tol_k)
 
 
-def test_bwd_deterministic(ea):
-    """No atomics: repeated runs are bitwise identical."""
-    q, k, v = (t.cuda() for t in make_qkv(1, 4, 700, 64, torch.bfloat16, seed=5, H_kv=2))
-    dout = make_dout(1, 4, 700, 64, torch.bfloat16, seed=5).cuda()
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_bwd_deterministic(ea, dtype):
+    """No atomics, partial sums added in a fixed order: repeated runs are
+    bitwise identical."""
+    q, k, v = (t.cuda() for t in make_qkv(1, 4, 700, 64, dtype, seed=5, H_kv=2))
+    dout = make_dout(1, 4, 700, 64, dtype, seed=5).cuda()
     o, lse = ea.fwd(q, k, v, causal=True)
     a = ea.bwd(q, k, v, o, lse, dout, causal=True)
     b = ea.bwd(q, k, v, o, lse, dout, causal=True)
