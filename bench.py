@@ -97,9 +97,17 @@ def cpu_baseline(w, q, k, v, n_slices: int):
     oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows, num_threads=threads)
     dt = time.perf_counter() - t0
     flops = attention_flops(1, n_slices, w.N, w.d, w.causal)
+    # One core: the first slice again, single-threaded (the per-core rate).
+    rows1 = np.arange(w.N, dtype=np.int64)
+    t1 = time.perf_counter()
+    oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows1, num_threads=1)
+    dt1 = time.perf_counter() - t1
+    flops1 = attention_flops(1, 1, w.N, w.d, w.causal)
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
             "sample": f"{n_slices} of {w.B * w.H} (b,h) slices, all {w.N} rows each "
-                      f"({flops / 1e9:.1f} GFLOP by the same convention), {dt:.2f} s wall"}
+                      f"({flops / 1e9:.1f} GFLOP by the same convention), {dt:.2f} s wall",
+            "per_core_value": flops1 / dt1 / 1e12,
+            "per_core_sample": f"slice 0 on one thread ({flops1 / 1e9:.2f} GFLOP), {dt1:.2f} s wall"}
 
 
 def cpu_baseline_bwd(w, q, k, v, dout, n_kv: int):
