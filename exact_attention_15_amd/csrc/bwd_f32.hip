@@ -5,10 +5,11 @@
 // dQ = scale dS K, dK = scale dS^T Q), with every product on
 // v_mfma_f32_32x32x2_f32: exact fp32 products, fp32 accumulation, nothing
 // rounded below fp32. Structure as in the 16-bit kernels: a row-statistic
-// kernel writes D into the caller's `delta`; a dK/dV kernel owns 128 keys
-// (32 per wave, K rows in VGPRs, the workgroup's V rows in LDS) and streams
-// 32-row Q / dO tiles; a dQ kernel owns 128 query rows (32 per wave, Q and
-// dO rows in VGPRs) and streams 32-key K / V tiles. Tiles go HBM -> LDS by
+// kernel writes D into the caller's `delta`; a dK/dV kernel owns a tile of
+// keys (32 per wave, K rows in VGPRs, the tile's V rows in LDS) and streams
+// 32-row Q / dO stages; a dQ kernel owns a tile of query rows (32 per wave,
+// Q and dO rows in VGPRs) and streams 32-key K / V stages. At d = 64 four
+// wave groups share an item's stages (see FLayout). Tiles go HBM -> LDS by
 // direct copies (16 bytes per lane).
 //
 // fp32 32x32x2 products take one value per lane: lane l supplies A[l%32][k]
