@@ -138,6 +138,25 @@ def test_workload_full_size(ea, oracle_lib, name):
            f"{name} ({len(rows)} sampled rows)", w.N)
 
 
+@pytest.mark.parametrize("dtype,d,n,causal", [
+    (torch.bfloat16, 64, 131072, True),
+    (torch.float16, 128, 65535, False),
+    (torch.float32, 64, 32768, True),
+], ids=["bf16-d64-128k-causal", "f16-d128-64k-ragged", "f32-d64-32k-causal"])
+def test_long_sequence(ea, oracle_lib, dtype, d, n, causal):
+    """Sequence lengths far past the workloads (one slice): positions and
+    offsets stay exact; sampled rows across the whole range, the last rows
+    (which see every key) included."""
+    q, k, v = make_qkv(1, 1, n, d, dtype, seed=5100 + d)
+    o, lse = _run_gpu(ea, q, k, v, causal, ea.default_scale(d))
+    rng = np.random.default_rng(n)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n),
+                                     rng.integers(0, n, 48)])).astype(np.int64)
+    o_ref, lse_ref = oracle_lib.attn_fwd_ref_rows(q, k, v, causal, ea.default_scale(d), rows)
+    _check(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, dtype,
+           f"N={n} d={d} {dtype} causal={causal} ({len(rows)} sampled rows)", n)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],
                          ids=["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
