@@ -171,6 +171,33 @@ def test_bwd_workload_full_size(ea, oracle_lib, name):
     assert torch.all(dk64.sum(dim=2).abs() <= tol_k)
 
 
+@pytest.mark.parametrize("dtype,n,H,H_kv", [
+    (torch.bfloat16, 32768, 2, 1),
+    (torch.float32, 16384, 1, 1),
+], ids=["bf16-32k-gqa2", "f32-16k"])
+def test_bwd_long_sequence(ea, dtype, n, H, H_kv):
+    """Sequence lengths far past the workloads, causal, d = 64: the oracle's
+    backward is too slow there, so the identities that hold at any size are
+    checked on every element sum: dK sums to zero over keys, dV sums to the
+    group's summed dO; and the gradients are finite."""
+    G = H // H_kv
+    q, k, v = (t.cuda() for t in make_qkv(1, H, n, 64, dtype, seed=9900 + n, H_kv=H_kv))
+    dout = make_dout(1, H, n, 64, dtype, seed=9900 + n).cuda()
+    o, lse = ea.fwd(q, k, v, causal=True)
+    dq, dk, dv = ea.bwd(q, k, v, o, lse, dout, causal=True)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.all(torch.isfinite(t.float()))
+    dk64, dv64, do64 = (t.to(torch.float64) for t in (dk, dv, dout))
+    dsum = do64.reshape(1, H_kv, G, n, 64).sum(dim=(2, 3))
+    tol_v = 4 * U[dtype] * do64.abs().reshape(1, H_kv, G, n, 64).sum(dim=(2, 3)) + 1e-3
+    err_v = float(((dv64.sum(dim=2) - dsum).abs() / tol_v).max())
+    tol_k = 4 * U[dtype] * dk64.abs().sum(dim=2) + 1e-3
+    err_k = float((dk64.sum(dim=2).abs() / tol_k).max())
+    print(f"N={n} {dtype}: identity errors / bounds: dv {err_v:.3f}, dk {err_k:.3f}", flush=True)
+    assert err_v <= 1 and err_k <= 1
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_bwd_deterministic(ea, dtype):
     """No atomics, partial sums added in a fixed order: repeated runs are
