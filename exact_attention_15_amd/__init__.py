@@ -37,7 +37,21 @@ def load_library():
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m exact_attention_15_amd.build` "
             "(or __graft_entry__.build()); there is no fallback implementation")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = _configure(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def load_probe_library():
+    """The race-check build (timing probes compiled in, same entry points),
+    for the tests that compare it with the library bit for bit."""
+    path = os.path.join(_PKG, "libattn_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_attention_15_amd.build`")
+    return _configure(ctypes.CDLL(path))
+
+
+def _configure(lib):
+    """Declare the C signatures of include/attn.h on a loaded library."""
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                              ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
@@ -55,7 +69,6 @@ def load_library():
     lib.attn_unfused_workspace_bytes.restype = i64
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

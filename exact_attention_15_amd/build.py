@@ -31,15 +31,29 @@ FLAGS = [
 ]
 
 
+# The race-check build: the same sources with timing probes compiled in
+# (ATTN_DELAY_PROBE), loaded only by the race tests, which compare its
+# outputs with the library's bit for bit.
+PROBE_LIB_PATH = os.path.join(PKG, "libattn_probe.so")
+
+
 def build_library(verbose: bool = False, extra_flags=None) -> str:
+    """Build libattn.so and the race-check libattn_probe.so (two hipcc runs
+    in parallel)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-           *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+    jobs = []
+    for path, defs in ((LIB_PATH, []), (PROBE_LIB_PATH, ["-DATTN_DELAY_PROBE=1"])):
+        tmp = path + ".tmp"
+        cmd = [HIPCC, *FLAGS, *defs, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
+               *srcs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((subprocess.Popen(cmd), tmp, path))
+    failed = [path for proc, _, path in jobs if proc.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, f"hipcc for {failed}")
+    for _, tmp, path in jobs:
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -79,6 +79,24 @@ struct UnfusedParams {
     float scale;
 };
 
+// Timing probe, compiled in only by the race-check build (ATTN_DELAY_PROBE):
+// at each marked point a third of the (wave, step, workgroup) combinations
+// sleep ~512 cycles, so the waves of a workgroup reach their barriers and
+// buffer reuses in orders the normal build does not produce. Nothing else
+// changes; results must stay bit-identical unless a buffer is overwritten
+// while another wave still reads it.
+#ifdef ATTN_DELAY_PROBE
+#define ATTN_PROBE(step)                                                                      \
+    do {                                                                                      \
+        const int probe_w_ = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);           \
+        if ((probe_w_ * 5 + (int)(step) * 3 + (int)blockIdx.x) % 3 == 0) __builtin_amdgcn_s_sleep(8); \
+    } while (0)
+#else
+#define ATTN_PROBE(step) \
+    do {                 \
+    } while (0)
+#endif
+
 // The fewest query rows any forward workgroup takes (fp32, d = 64); bounds
 // the one-dimensional grids.
 constexpr int kMinBlockM = 64;

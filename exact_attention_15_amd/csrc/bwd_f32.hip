@@ -318,6 +318,7 @@ __global__ __launch_bounds__(FLayout<D>::kThreads, 1) void bwd_dkdv_f32_kernel(B
             float nl = 0.f, nd = 0.f;
             const bool next = s + NG < n_steps;
             if (next) stage_issue(s + NG, par ^ 1, nl, nd);
+            ATTN_PROBE(it);
             if (s < n_steps) {
                 const int hh = s / n_t;
                 const int qs = (t0 + (s - hh * n_t)) * kFQStage;
@@ -325,6 +326,7 @@ __global__ __launch_bounds__(FLayout<D>::kThreads, 1) void bwd_dkdv_f32_kernel(B
             }
             __builtin_amdgcn_s_waitcnt(0x0f70);
             if (next) stage_publish(par ^ 1, nl, nd);
+            ATTN_PROBE(it + 1);
             __syncthreads();
         }
 
@@ -481,6 +483,7 @@ __global__ __launch_bounds__(FLayout<D>::kThreads, 1) void bwd_dq_f32_kernel(Bwd
                 Cp::copy(Kg, kv0 + NG * kFKStage, N, kL(par ^ 1), wq, coff);
                 Cp::copy(Vg, kv0 + NG * kFKStage, N, vL(par ^ 1), wq, coff);
             }
+            ATTN_PROBE(it);
             if (j < n_tiles && (!CAUSAL || kv0 <= qw + 31)) {
                 const LDS_AS char* kb = kL(par);
                 const LDS_AS char* vb = vL(par);
@@ -523,6 +526,7 @@ __global__ __launch_bounds__(FLayout<D>::kThreads, 1) void bwd_dq_f32_kernel(Bwd
                 }
             }
             __builtin_amdgcn_s_waitcnt(0x0f70);
+            ATTN_PROBE(it + 1);
             __syncthreads();
         }
 

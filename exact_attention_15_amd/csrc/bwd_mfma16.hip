@@ -303,6 +303,7 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
         const int s = GROUPS * i + grp;
         float nl = 0.f, nd = 0.f;
         if (s + GROUPS < n_steps) stage_issue(s + GROUPS, qL[1 - PAR], oL[1 - PAR], nl, nd);
+        ATTN_PROBE(i);
         if (GROUPS == 1 || s < n_steps) {   // one group: s < n_steps always
             const int hh = s / n_t;
             const int t = t0 + (s - hh * n_t);
@@ -316,6 +317,7 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
         }
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the next stage's copies and loads
         if (s + GROUPS < n_steps) stage_publish(lL[1 - PAR], dL[1 - PAR], nl, nd);
+        ATTN_PROBE(i + 1);
         __syncthreads();
     };
 
@@ -569,8 +571,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(BwdParams p) {
             Cp::copy(Kg, (j + 1) * kKStage, N, kL[1 - PAR], wave, coff);
             Cp::copy(Vg, (j + 1) * kKStage, N, vL[1 - PAR], wave, coff);
         }
+        ATTN_PROBE(j);
         if (j < n_live) tile_compute(j, kL[PAR], vL[PAR]);
         __builtin_amdgcn_s_waitcnt(0x0f70);
+        ATTN_PROBE(j + 1);
         __syncthreads();
     };
 

@@ -164,6 +164,7 @@ __global__ __launch_bounds__(kThreads) void fwd32_kernel(FwdParams p) {
             const int kv0 = j * kBlockN;
             const bool next = j + NG < n_tiles;
             if (next) load_tile(kv0 + NG * kBlockN);
+            ATTN_PROBE(it);
 
             const bool wave_live = j < n_tiles && (!CAUSAL || kv0 <= q0 + wave * 32 + 31);
             if (wave_live) {
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(kThreads) void fwd32_kernel(FwdParams p) {
                 }
             }
 
+            ATTN_PROBE(it + 1);
             if (next) store_tile(cur ^ 1);
             __syncthreads();
         }

@@ -469,10 +469,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
     // for its copies, which the next step reads).
     auto tile_steps = [&](int j, auto par_tag, auto has_pv_tag) __attribute__((always_inline)) {
         copies(j, par_tag);
+        ATTN_PROBE(j);
         mfma_step(j, par_tag, has_pv_tag);
+        ATTN_PROBE(j + 1);
         barrier();
         valu_step(j);
         if (grp == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+        ATTN_PROBE(j + 2);
         barrier();
     };
 

@@ -181,6 +181,7 @@ __global__ __launch_bounds__(kUThreads) void pv_kernel(UnfusedParams p) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 4; ++kb2) pb[kb2] = *(const u32x4*)(prow + t * 64 + 16 * kb2);
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the tile copy and P
+        ATTN_PROBE(t + 1);
         __syncthreads();
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -189,6 +190,7 @@ __global__ __launch_bounds__(kUThreads) void pv_kernel(UnfusedParams p) {
                 const LDS_AS char* rb = vL + 16 * kb2 * T::kRowBytes;
                 o[db] = Op::mfma(tr_read(rb + troff[db][0], rb + troff[db][1]), pb[kb2], o[db]);
             }
+        ATTN_PROBE(t);
         __syncthreads();   // every wave has read the tile before the next copy
     }
     if (qi < N) {
@@ -248,6 +250,7 @@ __global__ __launch_bounds__(kUThreads) void pv_f32_kernel(UnfusedParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) pb[4 * h + i] = *(const f32x4*)(prow + t * 64 + 32 * h + 4 * i);
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the tile copy and P
+        ATTN_PROBE(t + 1);
         __syncthreads();
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -259,6 +262,7 @@ __global__ __launch_bounds__(kUThreads) void pv_f32_kernel(UnfusedParams p) {
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32 * db], pb[4 * h + (tt >> 2)][tt & 3],
                                                                  o[db], 0, 0, 0);
             }
+        ATTN_PROBE(t);
         __syncthreads();   // every wave has read the tile before the next copy
     }
     if (qi < N) {

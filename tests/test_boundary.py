@@ -52,6 +52,16 @@ def test_attn_library_exports_header(attn_lib_path):
     ctypes.CDLL(attn_lib_path)   # loads without a GPU
 
 
+def test_probe_build_exports_the_same_entry_points(attn_lib_path):
+    """The race-check build (timing probes compiled in) is the same library:
+    the same exported functions, loadable without a GPU."""
+    from exact_attention_15_amd.build import PROBE_LIB_PATH, build_library
+    if not os.path.exists(PROBE_LIB_PATH):
+        build_library()
+    assert _exported(PROBE_LIB_PATH) == _exported(attn_lib_path)
+    ctypes.CDLL(PROBE_LIB_PATH)
+
+
 def test_oracle_library_exports_header(oracle_lib):
     decl = _declared_functions("attn_ref.h")
     assert decl == ["attn_bwd_ref", "attn_fwd_ref", "attn_fwd_ref_gqa", "attn_fwd_ref_rows",

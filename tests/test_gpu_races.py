@@ -1,0 +1,107 @@
+"""Race check: every entry point of the library against its timing-probe
+build (libattn_probe.so, the same sources with ATTN_DELAY_PROBE: at the
+marked points around each stage's copies and barriers, a third of the
+(wave, step, workgroup) combinations sleep ~512 cycles). Sleeping changes
+no arithmetic and no order of operations, only which wave reaches a barrier
+or a buffer first, so the outputs must be bit-identical; a difference would
+mean an LDS buffer overwritten while another wave still reads it, or a read
+before its copy landed."""
+import pytest
+import torch
+
+from exact_attention_15_amd.inputs import make_dout, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def libs():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_15_amd as ea
+    return ea, ea.load_library(), ea.load_probe_library()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _fwd(ea, lib, q, k, v, causal):
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    rc = lib.attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, H, k.shape[1], N, d, int(causal), ea.default_scale(d),
+                          ea.dtype_code(q.dtype), _stream())
+    assert rc == 0, rc
+    return o, lse
+
+
+def _bwd(ea, lib, q, k, v, o, lse, dout, causal):
+    B, H, N, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      delta.data_ptr(), B, H, k.shape[1], N, d, int(causal),
+                      ea.default_scale(d), ea.dtype_code(q.dtype), _stream())
+    assert rc == 0, rc
+    return dq, dk, dv, delta
+
+
+def _unfused(ea, lib, q, k, v, causal):
+    B, H, N, d = q.shape
+    code = ea.dtype_code(q.dtype)
+    ws = torch.empty(ea.unfused_workspace_bytes(B, H, N, code), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    rc = lib.attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), ws.data_ptr(), ws.numel(), B, H, N, d, int(causal),
+                              ea.default_scale(d), code, _stream())
+    assert rc == 0, rc
+    return o, lse
+
+
+def _same(a, b, what):
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y), what
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32],
+                         ids=["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_forward_matches_probe_build(libs, dtype, d, causal):
+    ea, lib, probe = libs
+    q, k, v = (t.cuda() for t in make_qkv(2, 4, 1777, d, dtype, seed=7300 + d, H_kv=2))
+    _same(_fwd(ea, lib, q, k, v, causal), _fwd(ea, probe, q, k, v, causal),
+          f"forward {dtype} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype,d,H,H_kv", [
+    (torch.bfloat16, 64, 4, 2),    # two wave groups per dK/dV item
+    (torch.bfloat16, 64, 4, 4),
+    (torch.float16, 128, 8, 1),    # split dK/dV partial sums and their reduction
+    (torch.float32, 64, 4, 2),     # four wave groups, paired tiles
+    (torch.float32, 128, 2, 2),
+], ids=["bf16-d64-gqa2", "bf16-d64-mha", "f16-d128-split", "f32-d64-gqa2", "f32-d128"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_backward_matches_probe_build(libs, dtype, d, H, H_kv, causal):
+    ea, lib, probe = libs
+    n = 1111
+    q, k, v = (t.cuda() for t in make_qkv(1, H, n, d, dtype, seed=7400 + d + H, H_kv=H_kv))
+    dout = make_dout(1, H, n, d, dtype, seed=7400 + d + H).cuda()
+    o, lse = _fwd(ea, lib, q, k, v, causal)
+    _same(_bwd(ea, lib, q, k, v, o, lse, dout, causal),
+          _bwd(ea, probe, q, k, v, o, lse, dout, causal),
+          f"backward {dtype} d={d} H={H} H_kv={H_kv} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_unfused_matches_probe_build(libs, dtype, d):
+    ea, lib, probe = libs
+    q, k, v = (t.cuda() for t in make_qkv(1, 3, 333, d, dtype, seed=7500 + d))
+    _same(_unfused(ea, lib, q, k, v, True), _unfused(ea, probe, q, k, v, True),
+          f"unfused {dtype} d={d}")
