@@ -19,7 +19,8 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_15_amd.inputs import WORKLOADS, make_qkv, make_structured_qkv, workload_inputs
+from exact_attention_15_amd.inputs import (WORKLOADS, make_dout, make_qkv, make_structured_qkv,
+                                           workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -230,6 +231,32 @@ def test_running_max_paths(ea, oracle_lib, kind, dtype, d, causal):
           f"{err_l:.3e} (bound {tol_l:.3e})", flush=True)
     assert np.all(np.isfinite(o)) and err_o <= O_TOL[dtype], err_o
     assert err_l <= tol_l, err_l
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_nonfinite_inputs_return_normally(ea, dtype):
+    """NaN and infinite inputs are outside the contract (the results are not
+    specified), but the calls return ATTN_OK and the stream stays usable:
+    no address in any kernel depends on the data. Rows of a slice whose
+    inputs are all finite still match the clean run."""
+    q, k, v = (t.cuda() for t in make_qkv(2, 2, 300, 64, dtype, seed=77))
+    dout = make_dout(2, 2, 300, 64, dtype, seed=77).cuda()
+    o_clean, lse_clean = ea.fwd(q, k, v, causal=True)
+    qb, kb, vb = q.clone(), k.clone(), v.clone()
+    qb[0, 0, 5, 3] = float("nan")
+    kb[0, 1, 7, 0] = float("inf")
+    vb[0, 0, 11, 2] = float("-inf")
+    o, lse = ea.fwd(qb, kb, vb, causal=True)
+    dq, dk, dv = ea.bwd(qb, kb, vb, o, lse, dout, causal=True)
+    o_u, _ = ea.fwd_unfused(qb, kb, vb, causal=True)
+    torch.cuda.synchronize()
+    # batch 1 holds no non-finite input: its slices are unaffected
+    assert torch.equal(o[1], o_clean[1]) and torch.equal(lse[1], lse_clean[1])
+    assert torch.isfinite(dq[1].float()).all() and torch.isfinite(dk[1].float()).all()
+    o2, _ = ea.fwd(q, k, v, causal=True)   # the stream still works
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o_clean)
+    del o_u, dv
 
 
 def test_deterministic(ea):
