@@ -45,9 +45,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"oracle library missing: {LIB_PATH}; run oracle.build()")
-    lib = ctypes.CDLL(LIB_PATH)
+    # ATTN_ORACLE_LIB: a library built from a deliberately altered copy of
+    # attn_ref.c, loaded only by the mutation test that checks the pins catch it.
+    path = os.environ.get("ATTN_ORACLE_LIB", LIB_PATH)
+    if not os.path.exists(path):
+        raise RuntimeError(f"oracle library missing: {path}; run oracle.build()")
+    lib = ctypes.CDLL(path)
     i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)
     lib.attn_fwd_ref.argtypes = [vp, vp, vp, dp, dp, i64, i64, i64, i64,
                                  ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int]
