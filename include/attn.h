@@ -1,10 +1,11 @@
 /*
- * attn.h — C ABI of the gfx950 (MI355X) exact attention forward library,
- * libattn.so.
+ * attn.h — C ABI of the gfx950 (MI355X) exact attention library, libattn.so.
  *
  * The operation is the fused, tiled attention forward pass
  *     O = softmax(scale * Q K^T [+ causal mask]) V
- * together with the per-row log-sum-exp of the scaled scores.
+ * together with the per-row log-sum-exp of the scaled scores; also its
+ * grouped-query form, its gradients, and the unfused three-kernel forward
+ * kept as the comparison path.
  *
  * Sources (cited by page title and section):
  *   [naive-attn]  cishoon.github.io, "flashattention" post, section 1.1.2:
@@ -131,7 +132,8 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* ls
  *              once (nearest even) from fp32; fp32 rounds nothing below fp32.
  * stream       hipStream_t (NULL = the null stream).
  *
- * Asynchronous: three kernels are enqueued on `stream` and the call returns;
+ * Asynchronous: three kernels (four when f16/bf16 dk/dv work is split over
+ * query-head groups) are enqueued on `stream` and the call returns;
  * no host synchronisation, no device allocation, no atomics (results do not
  * depend on scheduling). Validation precedes any HIP call. Outputs must not
  * alias inputs or each other.
