@@ -7,7 +7,8 @@ Default workload: bf16, causal, B=4, H=16, N=4096, d=64.
 Prints ONE JSON line with the attention TFLOPS, its roofline fraction and
 the CPU fp64 oracle timed on a bounded sample of the same workload.
 ``--pass bwd`` times the backward pass (dQ, dK, dV) instead: one step is one
-attn_bwd call (its three kernels) with q, k, v, o, lse and dO resident.
+attn_bwd call (its three or four kernels) with q, k, v, o, lse and dO
+resident.
 ``--pass unfused`` times the unfused three-kernel forward (S, softmax, P V
 with N x N buffers) and, on the same inputs, the fused kernel, and reports
 what fusion gains.
@@ -35,6 +36,11 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
 DTYPE_NAME = {"torch.bfloat16": "bf16", "torch.float16": "fp16", "torch.float32": "fp32"}
+
+# Work of the CPU baseline: the multi-core sample (whole (b,h) slices; all 64
+# of the headline workload, ~5-15 s on 16 cores) and the single-thread one.
+CPU_FLOPS = 150e9
+PER_CORE_FLOPS = 2e9
 
 COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_counters.txt")
 # Sources of the kernel the committed counters were taken on (the bf16 /
@@ -97,17 +103,24 @@ def cpu_baseline(w, q, k, v, n_slices: int):
     oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows, num_threads=threads)
     dt = time.perf_counter() - t0
     flops = attention_flops(1, n_slices, w.N, w.d, w.causal)
-    # One core: the first slice again, single-threaded (the per-core rate).
-    rows1 = np.arange(w.N, dtype=np.int64)
+    # One core: the last rows of slice 0 (they see every key), single-threaded,
+    # about PER_CORE_FLOPS of the rows' own products (4 d FLOP per visible key).
+    rows1, flops1 = [], 0.0
+    for i in range(w.N - 1, -1, -1):
+        rows1.append(i)
+        flops1 += 4.0 * w.d * (i + 1 if w.causal else w.N)
+        if flops1 >= PER_CORE_FLOPS:
+            break
     t1 = time.perf_counter()
-    oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows1, num_threads=1)
+    oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, np.array(rows1, dtype=np.int64),
+                             num_threads=1)
     dt1 = time.perf_counter() - t1
-    flops1 = attention_flops(1, 1, w.N, w.d, w.causal)
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
             "sample": f"{n_slices} of {w.B * w.H} (b,h) slices, all {w.N} rows each "
                       f"({flops / 1e9:.1f} GFLOP by the same convention), {dt:.2f} s wall",
             "per_core_value": flops1 / dt1 / 1e12,
-            "per_core_sample": f"slice 0 on one thread ({flops1 / 1e9:.2f} GFLOP), {dt1:.2f} s wall"}
+            "per_core_sample": f"the last {len(rows1)} rows of slice 0 on one thread "
+                               f"({flops1 / 1e9:.2f} GFLOP), {dt1:.2f} s wall"}
 
 
 def cpu_baseline_bwd(w, q, k, v, dout, n_kv: int):
@@ -381,7 +394,8 @@ def main():
                          "forward against the fused one")
     ap.add_argument("--cpu-slices", type=int, default=None,
                     help="slices the CPU oracle baseline runs on: (b,h) slices for the forward "
-                         "(default 64), K/V slices for the backward (default 4)")
+                         "(default: as many as fit 150 GFLOP, all 64 of the headline workload), "
+                         "K/V slices for the backward (default 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity gate")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -499,7 +513,8 @@ def main():
         "wall_s_timed_region": round(t_wall, 4),
     }
     if not args.no_cpu_baseline:
-        n_sl = max(1, min(args.cpu_slices or 64, w.B * w.H))
+        per_slice = attention_flops(1, 1, w.N, w.d, w.causal)
+        n_sl = max(1, min(args.cpu_slices or int(CPU_FLOPS // per_slice), w.B * w.H))
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, n_sl)
     print(json.dumps(line), flush=True)
 
