@@ -256,10 +256,11 @@ def median_launch_ms(fn, n: int = 200) -> float:
     return ts[n // 2]
 
 
-def gfx_clock_under_load(fn, seconds: float = 0.3):
+def gfx_clock_under_load(fn, seconds: float = 0.3, ms_per_call: float = 0.1):
     """Median GFX clock (MHz, from amdsmi) sampled while launches of fn keep
-    the GPU busy (outside the timed region); None where amdsmi is missing or
-    refuses."""
+    the GPU busy (outside the timed region): ~25 ms of launches are queued
+    before each reading, and a reading counts only if the stream still has
+    work pending after it. None where amdsmi is missing or refuses."""
     import torch
     try:
         import amdsmi
@@ -269,15 +270,16 @@ def gfx_clock_under_load(fn, seconds: float = 0.3):
         return None
     clocks = []
     try:
+        stream = torch.cuda.current_stream()
+        per_sample = max(10, int(25.0 / max(ms_per_call, 1e-3)))
         t_end = time.perf_counter() + seconds
-        for _ in range(20):   # queue work ahead of the first sample
-            fn()
         while time.perf_counter() < t_end:
-            for _ in range(10):
+            for _ in range(per_sample):
                 fn()
             info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
             clk = info.get("clk") if isinstance(info, dict) else None
-            if isinstance(clk, (int, float)) and clk > 0:
+            busy = not stream.query()
+            if busy and isinstance(clk, (int, float)) and clk > 0:
                 clocks.append(float(clk))
         torch.cuda.synchronize()
     except Exception:
@@ -476,7 +478,7 @@ def main():
     ms = start.elapsed_time(stop) / args.steps
     step_fn = lambda: ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out)   # noqa: E731
     ms_median = median_launch_ms(step_fn)
-    clock = gfx_clock_under_load(step_fn)
+    clock = gfx_clock_under_load(step_fn, ms_per_call=ms_median)
 
     flops = attention_flops(w.B, w.H, w.N, w.d, w.causal)
     tflops = flops / (ms * 1e-3) / 1e12
