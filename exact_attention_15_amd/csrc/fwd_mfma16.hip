@@ -24,8 +24,12 @@
 //          chunks here, instead of padding).
 //
 // gfx950 design (not the pages'):
-//   * 512 threads = 8 wave64s; each wave owns QB blocks of 32 query rows
-//     (QB = 2 for d = 64, 1 for d = 128). K/V tiles hold 64 keys.
+//   * 512 threads = 8 wave64s; each wave owns QB blocks of 32 query rows,
+//     QB = 1 or 2 (2 only at d = 64, where the registers hold two blocks).
+//     The launcher takes QB = 2 for long non-causal runs (twice the reuse of
+//     every K/V fragment) and QB = 1 under a causal mask (half as many
+//     diagonal tiles per work item) or when QB = 2 would leave compute units
+//     without a work item. K/V tiles hold 64 keys.
 //   * Both products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32
 //     accumulation, in transposed form so that one lane owns one query:
 //        S^T[key][query] = K . Q^T     (A = K rows from LDS, B = Q in VGPRs)
@@ -81,13 +85,11 @@ constexpr int kThreads = 512;               // 8 waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kCopyWaves = 4;               // group A issues the HBM -> LDS copies
 
-template <int D>
-struct QueryBlocks {
-    static constexpr int value = D == 64 ? 2 : 1;   // 32-row query blocks per wave
-};
+constexpr int kComputeUnits = 256;         // MI355X
 
-template <int D>
-constexpr int block_m() { return kWaves * 32 * QueryBlocks<D>::value; }
+// Query rows per work item with QB 32-row blocks per wave.
+template <int QB>
+constexpr int block_m() { return kWaves * 32 * QB; }
 
 // LDS layout of one K or V tile: 64 rows of D 16-bit values, row-major, with
 // 16-byte chunk c of row r stored at chunk c ^ swz(r).
@@ -175,12 +177,12 @@ __device__ __forceinline__ float permlane16_swap_y(float x, float y) {
     return __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-template <bool IS_BF16, int D, bool CAUSAL>
+template <bool IS_BF16, int D, bool CAUSAL, int QB>
 __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
+    static_assert(QB == 1 || (QB == 2 && D == 64), "two query blocks per wave only at d = 64");
     using Op = Op16<IS_BF16>;
     using T = Tile<D>;
-    constexpr int QB = QueryBlocks<D>::value;
-    constexpr int BM = block_m<D>();
+    constexpr int BM = block_m<QB>();
     constexpr int NKD = D / 16;   // QK^T contraction steps
     constexpr int NDB = D / 32;   // 32-row blocks of O^T
 
@@ -291,11 +293,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
         for (int kb2 = 0; kb2 < 4; ++kb2) pk[qb][kb2] = u32x4{0u, 0u, 0u, 0u};
     }
 
-    // Row maxima and rescale decisions of the current tile. At d = 64 the
-    // VALU step is the longer of the two steps, so they are taken in the
-    // MFMA step (they need only S); at d = 128 the MFMA step is the longer
-    // one and they stay in the VALU step.
-    constexpr bool kMaxInMfmaStep = D == 64;
+    // Row maxima and rescale decisions of the current tile. With two query
+    // blocks the VALU step is the longer of the two steps, so they are taken
+    // in the MFMA step (they need only S); with one block the MFMA step is
+    // the longer one and they stay in the VALU step (both measured).
+    constexpr bool kMaxInMfmaStep = QB == 2;
     float m_old[QB];
     bool need[QB];
     // Scores past the causal diagonal or past N become -inf; then the row
@@ -521,12 +523,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
     }
 }
 
-template <bool IS_BF16, int D, bool CAUSAL>
-hipError_t launch(FwdParams p, hipStream_t s) {
-    p.n_qtiles = (int)((p.N + block_m<D>() - 1) / block_m<D>());
+template <bool IS_BF16, int D, bool CAUSAL, int QB>
+hipError_t launch_qb(FwdParams p, hipStream_t s) {
+    p.n_qtiles = (int)((p.N + block_m<QB>() - 1) / block_m<QB>());
     const dim3 grid((unsigned)(p.n_qtiles * p.BH));
-    hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL, QB>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
+}
+
+// Two query blocks per wave only without a causal mask, at d = 64, and when
+// their work items still cover every compute unit (measured: +2.5 to +6 %
+// on long non-causal runs; under a causal mask one block is 3 % faster at
+// the causal workloads, and on short sequences one block is up to 50 %
+// faster through the doubled item count).
+template <bool IS_BF16, int D, bool CAUSAL>
+hipError_t launch(const FwdParams& p, hipStream_t s) {
+    if constexpr (D == 64 && !CAUSAL) {
+        const int64_t items2 = (p.N + block_m<2>() - 1) / block_m<2>() * p.BH;
+        if (items2 >= kComputeUnits) return launch_qb<IS_BF16, D, CAUSAL, 2>(p, s);
+    }
+    return launch_qb<IS_BF16, D, CAUSAL, 1>(p, s);
 }
 
 }  // namespace
