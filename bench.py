@@ -256,11 +256,13 @@ def median_launch_ms(fn, n: int = 200) -> float:
     return ts[n // 2]
 
 
-def gfx_clock_under_load(fn, seconds: float = 0.3, ms_per_call: float = 0.1):
-    """Median GFX clock (MHz, from amdsmi) sampled while launches of fn keep
-    the GPU busy (outside the timed region): ~25 ms of launches are queued
-    before each reading, and a reading counts only if the stream still has
-    work pending after it. None where amdsmi is missing or refuses."""
+def gfx_clock_under_load(fn, seconds: float = 2.0, ms_per_call: float = 0.1):
+    """Median GFX clock (MHz, from amdsmi) while launches of fn keep the GPU
+    busy (outside the timed region). amdsmi's readings trail the load by up
+    to about a second, so launches run without a break for `seconds` and
+    only readings from the second half count, each taken with ~25 ms of
+    launches queued and kept only while the stream still has work pending.
+    None where amdsmi is missing or refuses."""
     import torch
     try:
         import amdsmi
@@ -272,10 +274,12 @@ def gfx_clock_under_load(fn, seconds: float = 0.3, ms_per_call: float = 0.1):
     try:
         stream = torch.cuda.current_stream()
         per_sample = max(10, int(25.0 / max(ms_per_call, 1e-3)))
-        t_end = time.perf_counter() + seconds
-        while time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
             for _ in range(per_sample):
                 fn()
+            if time.perf_counter() - t0 < seconds / 2:
+                continue
             info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
             clk = info.get("clk") if isinstance(info, dict) else None
             busy = not stream.query()
