@@ -139,6 +139,20 @@ def test_workload_full_size(ea, oracle_lib, name):
            f"{name} ({len(rows)} sampled rows)", w.N)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_two_query_block_kernel(ea, oracle_lib, dtype):
+    """The non-causal d = 64 kernel with two 32-row query blocks per wave,
+    which the launcher takes only when its 512-row items cover every compute
+    unit (here 2*64 slices x 2 tiles = 256 items, N ragged past a tile):
+    sampled rows against the oracle."""
+    q, k, v = make_qkv(2, 64, 1000, 64, dtype, seed=5200)
+    o, lse = _run_gpu(ea, q, k, v, False, ea.default_scale(64))
+    rows = _sample_rows(2, 64, 1000, np.random.default_rng(5200), n_random=96)
+    o_ref, lse_ref = oracle_lib.attn_fwd_ref_rows(q, k, v, False, ea.default_scale(64), rows)
+    _check(o.reshape(-1, 64)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, dtype,
+           f"two query blocks N=1000 {dtype} ({len(rows)} sampled rows)", 1000)
+
+
 @pytest.mark.parametrize("dtype,d,n,causal", [
     (torch.bfloat16, 64, 131072, True),
     (torch.float16, 128, 65535, False),

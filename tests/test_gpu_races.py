@@ -79,6 +79,16 @@ def test_forward_matches_probe_build(libs, dtype, d, causal):
           f"forward {dtype} d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_forward_two_query_blocks_matches_probe_build(libs, dtype):
+    """A non-causal grid large enough for the two-query-block kernel (512
+    query rows per item at d = 64; 2*64 slices x 2 tiles = 256 items)."""
+    ea, lib, probe = libs
+    q, k, v = (t.cuda() for t in make_qkv(2, 64, 1024, 64, dtype, seed=7350))
+    _same(_fwd(ea, lib, q, k, v, False), _fwd(ea, probe, q, k, v, False),
+          f"forward two query blocks {dtype}")
+
+
 @pytest.mark.parametrize("dtype,d,H,H_kv", [
     (torch.bfloat16, 64, 4, 2),    # two wave groups per dK/dV item
     (torch.bfloat16, 64, 4, 4),
