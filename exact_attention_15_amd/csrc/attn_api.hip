@@ -93,7 +93,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.BH_kv = (int)(B * H_kv);
     p.H_kv = (int)H_kv;
     p.G = (int)(H / H_kv);
-    p.splits = 1;   // chosen by the launcher
+    p.chunk = 0;    // chosen by the launcher
     p.scale = scale;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 

@@ -58,7 +58,7 @@ struct BwdParams {
     int BH_kv;          // B * H_kv key/value slices
     int H_kv;
     int G;              // H / H_kv
-    int splits;         // query-head splits per K/V head (partial dK, dV in dq's memory when > 1)
+    int chunk;          // steps per dK/dV item when > 0 (partial dK, dV in dq's memory), else whole key tiles
     float scale;        // multiplied into dQ and dK
     float scale_log2;   // scale * log2(e)
 };

@@ -1,0 +1,145 @@
+// bwd_chunks.h — how the dK/dV work of the 16-bit backward pass is dealt out
+// as workgroup items.
+//
+// The dK/dV work of one key tile (kKeyBlock keys of one K/V slice) is a
+// sequence of steps, one per (query head of the K/V head's group, query tile
+// of kQStage rows that can see the keys), head-major. Without grouped-query
+// heads an item is a whole key tile. With G query heads per K/V head the
+// items become G times fewer and longer, and under a causal mask key tile kt
+// has (n_qs - 2 kt) G steps, so one round of items is as long as its first
+// key tile. Then every key tile's steps are cut into chunks of one length
+// L (the last chunk of a tile shorter), each chunk an item of its own that
+// writes fp32 partial sums of dK^T and dV^T; a reduction adds a tile's
+// chunks in chunk order (deterministic) into dK and dV.
+//
+// Partial sums live in dq's memory (2 G N D bytes per K/V slice for
+// f16/bf16, written by the last kernel only). Chunk c of key tile kt holds
+// rows(kt) partial rows (of 2 D floats: dK^T and dV^T) per K/V slice, so the
+// plan must satisfy  sum_kt n_chunks(kt) rows(kt) * 8 D <= 2 G N D, i.e.
+// sum_kt n_chunks(kt) rows(kt) <= G N / 4, which needs G >= 4.
+//
+// Layout of the partials (floats from the start of dq's memory), chunk c of
+// key tile kt, K/V slice s, key row r < rows(kt), column j < D:
+//   block = (first(kt) kKeyBlock + c rows(kt)) BH_kv 2D + s rows(kt) 2D
+//   dK^T partial at block + r D + j, dV^T partial at block + (rows(kt) + r) D + j
+// with first(kt) the chunks of the earlier key tiles; as every key tile but
+// the last has kKeyBlock rows, the blocks tile the rows without overlap.
+//
+// Plain constexpr functions: the kernels call them on device, the launcher on
+// the host, and a host test compiles this header with g++ alone.
+#ifndef ATTN_BWD_CHUNKS_H
+#define ATTN_BWD_CHUNKS_H
+
+#include <stdint.h>
+
+namespace attn {
+namespace bwdplan {
+
+constexpr int kKeyBlock = 128;   // keys per dK/dV item (4 waves x 32)
+constexpr int kQStage = 64;      // query rows per step
+
+constexpr int n_query_stages(int64_t N) { return (int)((N + kQStage - 1) / kQStage); }
+constexpr int n_key_tiles(int64_t N) { return (int)((N + kKeyBlock - 1) / kKeyBlock); }
+
+// Steps of key tile kt of one K/V slice.
+constexpr int kv_steps(int G, int n_qs, int kt, bool causal) {
+    return G * (causal ? n_qs - kt * (kKeyBlock / kQStage) : n_qs);
+}
+
+// Keys of key tile kt (kKeyBlock except for a ragged last tile).
+constexpr int tile_rows(int64_t N, int kt) {
+    const int64_t left = N - (int64_t)kt * kKeyBlock;
+    return left < kKeyBlock ? (int)left : kKeyBlock;
+}
+
+constexpr int n_chunks(int steps, int chunk) { return (steps + chunk - 1) / chunk; }
+
+// Item number w (over all K/V slices, key tile major, then chunk, then slice)
+// of a chunked plan.
+struct Item {
+    int kt;      // key tile
+    int slice;   // K/V slice b * H_kv + h_kv
+    int s0;      // first step
+    int s1;      // one past the last step
+    int64_t part_row;   // first(kt) kKeyBlock + c rows(kt): the block's row offset
+    bool valid;  // w lies inside the plan
+};
+
+constexpr Item locate(int w, int64_t N, int G, int BH_kv, bool causal, int chunk) {
+    Item it{0, 0, 0, 0, 0, false};
+    const int n_qs = n_query_stages(N);
+    const int n_kt = n_key_tiles(N);
+    int rem = w / BH_kv;
+    it.slice = w - rem * BH_kv;
+    int first = 0;
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int steps = kv_steps(G, n_qs, kt, causal);
+        const int nc = n_chunks(steps, chunk);
+        if (rem < nc) {
+            it.kt = kt;
+            it.s0 = rem * chunk;
+            it.s1 = it.s0 + chunk < steps ? it.s0 + chunk : steps;
+            it.part_row = (int64_t)first * kKeyBlock + (int64_t)rem * tile_rows(N, kt);
+            it.valid = true;
+            return it;
+        }
+        rem -= nc;
+        first += nc;
+    }
+    return it;
+}
+
+// Chunks of the key tiles before kt (the reduction's view of the plan).
+constexpr int first_chunk(int kt, int64_t N, int G, bool causal, int chunk) {
+    const int n_qs = n_query_stages(N);
+    int first = 0;
+    for (int k = 0; k < kt; ++k) first += n_chunks(kv_steps(G, n_qs, k, causal), chunk);
+    return first;
+}
+
+// Items of a plan with chunk length `chunk` (all K/V slices).
+constexpr int64_t plan_items(int64_t N, int G, int BH_kv, bool causal, int chunk) {
+    const int n_qs = n_query_stages(N);
+    int64_t n = 0;
+    for (int kt = 0; kt < n_key_tiles(N); ++kt) n += n_chunks(kv_steps(G, n_qs, kt, causal), chunk);
+    return n * BH_kv;
+}
+
+// Partial rows per K/V slice: sum_kt n_chunks(kt) rows(kt).
+constexpr int64_t plan_partial_rows(int64_t N, int G, bool causal, int chunk) {
+    const int n_qs = n_query_stages(N);
+    int64_t rows = 0;
+    for (int kt = 0; kt < n_key_tiles(N); ++kt)
+        rows += (int64_t)n_chunks(kv_steps(G, n_qs, kt, causal), chunk) * tile_rows(N, kt);
+    return rows;
+}
+
+// The chunk length for a call, or 0 for one item per key tile (partials not
+// used). Aims at about `target` items, the workgroups the device holds at
+// once; takes the shortest chunk whose partials fit dq's memory; keeps whole
+// key tiles unless chunks cut the longest item to at most 3/4 of its steps.
+constexpr int choose_chunk(int64_t N, int G, int BH_kv, bool causal, int target) {
+    const int n_qs = n_query_stages(N);
+    const int longest = kv_steps(G, n_qs, 0, causal);
+    int64_t total = 0;
+    for (int kt = 0; kt < n_key_tiles(N); ++kt) total += kv_steps(G, n_qs, kt, causal);
+    total *= BH_kv;
+    const int64_t lo64 = (total + target - 1) / target;
+    const int hi = (3 * (int64_t)longest) / 4;
+    if (lo64 > hi || hi < 1) return 0;
+    const int64_t cap_rows = (int64_t)G * N / 4;
+    if (plan_partial_rows(N, G, causal, hi) > cap_rows) return 0;
+    int lo = lo64 < 1 ? 1 : (int)lo64;
+    int top = hi;   // fits; find the smallest chunk in [lo, top] that fits
+    while (lo < top) {
+        const int mid = lo + (top - lo) / 2;
+        if (plan_partial_rows(N, G, causal, mid) <= cap_rows) top = mid;
+        else lo = mid + 1;
+    }
+    return top;
+}
+
+}  // namespace bwdplan
+}  // namespace attn
+
+#endif  // ATTN_BWD_CHUNKS_H

@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "attn_internal.h"
+#include "bwd_chunks.h"
 #include "mfma_common.h"
 
 namespace attn {
@@ -57,8 +58,11 @@ constexpr int kBwdThreads = 256;   // 4 waves
 constexpr int kBwdWaves = kBwdThreads / 64;
 constexpr int kKeyBlock = kBwdWaves * 32;     // keys per dK/dV workgroup
 constexpr int kQStage = 64;                   // query rows per LDS stage (dK/dV kernel)
+static_assert(kKeyBlock == bwdplan::kKeyBlock && kQStage == bwdplan::kQStage,
+              "the dK/dV item plan uses the kernel's tile sizes");
 constexpr int kQueryBlock = kBwdWaves * 32;   // query rows per dQ workgroup
 constexpr int kKStage = 64;                   // keys per LDS stage (dQ kernel)
+constexpr int kDkdvItems = 512;               // dK/dV workgroups resident at once (2 per CU)
 
 // 16-bit value to fp32.
 template <bool IS_BF16>
@@ -97,10 +101,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_delta_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// (2) dK, dV. Work item: (key tile of 128, b*H_kv + h_kv). Causal items are
-// ordered key tile 0 first: it is seen by the most query rows. The item's
-// query steps (every query tile of every query head of the group that can
-// see the keys) are dealt round-robin to GROUPS groups of 4 waves, each with
+// (2) dK, dV. Work item: (key tile of 128, b*H_kv + h_kv), or, when p.chunk > 0,
+// a chunk of p.chunk consecutive steps of such a key tile (bwd_chunks.h);
+// causal items are ordered key tile 0 first: it is seen by the most query
+// rows. The item's query steps (query tiles of the query heads of the group
+// that can see the keys, head-major) are dealt round-robin to GROUPS groups
+// of 4 waves, each with
 // its own LDS stage buffers and its own partial dK, dV for the same 128
 // keys; the partials are summed through LDS at the end. Two groups halve the
 // sequential length of an item at no extra traffic; they are used for
@@ -147,20 +153,31 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     LDS_AS float* const dL[2] = {(LDS_AS float*)d_lds0 + grp * kQStage,
                                  (LDS_AS float*)d_lds1 + grp * kQStage};
 
-    // Item w: key tile kt, K/V slice kv_bh, query-head split sp (of p.splits).
+    // Item w: key tile kt of K/V slice kv_bh, its steps s0 .. s0 + n_steps - 1.
     const int w = blockIdx.x;
-    const int per_kt = p.BH_kv * p.splits;
-    const int kt = w / per_kt;
-    const int rem = w - kt * per_kt;
-    const int sp = rem / p.BH_kv;
-    const int kv_bh = rem - sp * p.BH_kv;
+    const int n_qt = (N + kQStage - 1) / kQStage;
+    int kt, kv_bh, s0, n_steps;
+    int64_t part_row = 0;
+    if (p.chunk > 0) {
+        const bwdplan::Item it = bwdplan::locate(w, N, p.G, p.BH_kv, CAUSAL, p.chunk);
+        if (!it.valid) return;   // (the grid holds exactly the plan's items)
+        kt = it.kt;
+        kv_bh = it.slice;
+        s0 = it.s0;
+        n_steps = it.s1 - it.s0;
+        part_row = it.part_row;
+    } else {
+        kt = w / p.BH_kv;
+        kv_bh = w - kt * p.BH_kv;
+        s0 = 0;
+        n_steps = bwdplan::kv_steps(p.G, n_qt, kt, CAUSAL);
+    }
     const int k0 = kt * kKeyBlock;
     const int kw = k0 + 32 * wk;                 // first key of this wave
     const int key = kw + l32;                    // this lane's key
     const size_t kv_base = (size_t)kv_bh * (size_t)N * D;
-    // This item's query heads: Gs of the K/V head's G (b*H + h_kv*G + sp*Gs + ...).
-    const int Gs = p.G / p.splits;
-    const int bh0 = kv_bh * p.G + sp * Gs;
+    // The K/V head's query heads: b*H + h_kv*G + 0 .. G-1.
+    const int bh0 = kv_bh * p.G;
 
     // K and V fragments (B operands of S = Q K^T and dP = dO V^T): lane l
     // holds row key, elements 16kd + 8g .. +7. Keys past N read as zero.
@@ -188,10 +205,8 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     int coff[Cp::kPerWave];
     Cp::offsets(wk, lane, coff);
 
-    const int n_qt = (N + kQStage - 1) / kQStage;
     const int t0 = CAUSAL ? k0 / kQStage : 0;    // first query tile that sees these keys
     const int n_t = n_qt - t0;
-    const int n_steps = Gs * n_t;
     const int n_iter = (n_steps + GROUPS - 1) / GROUPS;   // steps GROUPS*i + grp
     const float c2 = p.scale_log2;
 
@@ -204,11 +219,12 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
             dv[db][i] = 0.f;
         }
 
-    // Step s: query head bh0 + s / n_t, query tile t0 + s % n_t.
+    // Item step s is step s0 + s of the key tile: query head bh0 + (s0 + s) / n_t,
+    // query tile t0 + (s0 + s) % n_t.
     auto stage_issue = [&](int s, LDS_AS char* qbuf, LDS_AS char* obuf, float& nl, float& nd)
         __attribute__((always_inline)) {
-        const int hh = s / n_t;
-        const int t = t0 + (s - hh * n_t);
+        const int hh = (s0 + s) / n_t;
+        const int t = t0 + (s0 + s - hh * n_t);
         const size_t base = (size_t)(bh0 + hh) * (size_t)N;
         Cp::copy((const uint16_t*)p.q + base * D, t * kQStage, N, qbuf, wk, coff);
         Cp::copy((const uint16_t*)p.dout + base * D, t * kQStage, N, obuf, wk, coff);
@@ -305,8 +321,8 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
         if (s + GROUPS < n_steps) stage_issue(s + GROUPS, qL[1 - PAR], oL[1 - PAR], nl, nd);
         ATTN_PROBE(i);
         if (GROUPS == 1 || s < n_steps) {   // one group: s < n_steps always
-            const int hh = s / n_t;
-            const int t = t0 + (s - hh * n_t);
+            const int hh = (s0 + s) / n_t;
+            const int t = t0 + (s0 + s - hh * n_t);
 #pragma unroll
             for (int qb = 0; qb < kQStage / 32; ++qb) {
                 const int qs = t * kQStage + 32 * qb;
@@ -368,15 +384,15 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     }
 
     // dK = scale dK^T^T, dV = dV^T^T: lane l writes key `key`, entries
-    // d = 32 db + 8 i4 + 4g .. +3. With query-head splits the fp32 partial
-    // sums go to dq's memory instead ([split][dK, dV][B*H_kv][N][D], not yet
-    // scaled); bwd_kv_reduce_kernel adds them up before dq is written.
-    if (p.splits > 1) {
+    // d = 32 db + 8 i4 + 4g .. +3. A chunk item writes fp32 partial sums
+    // (not yet scaled) into dq's memory instead, in the layout of
+    // bwd_chunks.h; bwd_kv_reduce_kernel adds them up before dq is written.
+    if (p.chunk > 0) {
         if (key < N) {
-            float* part = (float*)p.dq;
-            const size_t plane = (size_t)p.BH_kv * (size_t)N * D;
-            float* pk = part + (size_t)(2 * sp + 0) * plane + kv_base + (size_t)key * D;
-            float* pv = part + (size_t)(2 * sp + 1) * plane + kv_base + (size_t)key * D;
+            const int rows = bwdplan::tile_rows(N, kt);
+            float* blk = (float*)p.dq + ((size_t)part_row * p.BH_kv + (size_t)kv_bh * rows) * (2 * D);
+            float* pk = blk + (size_t)(key - k0) * D;
+            float* pv = blk + (size_t)(rows + key - k0) * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -410,19 +426,35 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
 }
 
 // ---------------------------------------------------------------------------
-// (2b) With query-head splits: dK = scale * sum of the splits' partial dK^T,
-// dV = sum of the partial dV^T, in split order (deterministic); 4 elements
-// per thread.
-template <bool IS_BF16>
-__global__ __launch_bounds__(kBwdThreads) void bwd_kv_reduce_kernel(BwdParams p, int64_t plane) {
+// (2b) Chunked dK/dV: dK = scale * the sum of a key tile's partial dK^T,
+// dV = the sum of its partial dV^T, added in chunk order (deterministic).
+// Workgroup: RW rows of key tile kt of K/V slice `slice`, 4 columns a thread.
+template <bool IS_BF16, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_kv_reduce_kernel(BwdParams p, bool causal) {
     using Op = Op16<IS_BF16>;
-    const int64_t e4 = ((int64_t)blockIdx.x * kBwdThreads + threadIdx.x) * 4;
-    if (e4 >= plane) return;
+    constexpr int TPR = D / 4;                 // threads per row
+    constexpr int RW = kBwdThreads / TPR;      // rows per workgroup
+    constexpr int WPT = kKeyBlock / RW;        // workgroups per key tile
+    const int N = (int)p.N;
+    const int w = blockIdx.x;
+    const int kt = w / (WPT * p.BH_kv);
+    const int rem = w - kt * (WPT * p.BH_kv);
+    const int rb = rem / p.BH_kv;
+    const int slice = rem - rb * p.BH_kv;
+    const int rows = bwdplan::tile_rows(N, kt);
+    const int r = rb * RW + (int)threadIdx.x / TPR;
+    const int j = 4 * ((int)threadIdx.x % TPR);
+    if (r >= rows) return;
+    const int n_qt = bwdplan::n_query_stages(N);
+    const int first = bwdplan::first_chunk(kt, N, p.G, causal, p.chunk);
+    const int nc = bwdplan::n_chunks(bwdplan::kv_steps(p.G, n_qt, kt, causal), p.chunk);
     const float* part = (const float*)p.dq;
     f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < p.splits; ++sp) {
-        const f32x4 a = *(const f32x4*)(part + (2 * sp + 0) * plane + e4);
-        const f32x4 b = *(const f32x4*)(part + (2 * sp + 1) * plane + e4);
+    for (int c = 0; c < nc; ++c) {
+        const size_t blk = ((size_t)((int64_t)first * kKeyBlock + (int64_t)c * rows) * p.BH_kv +
+                            (size_t)slice * rows) * (2 * D);
+        const f32x4 a = *(const f32x4*)(part + blk + (size_t)r * D + j);
+        const f32x4 b = *(const f32x4*)(part + blk + (size_t)(rows + r) * D + j);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             sk[x] += a[x];
@@ -430,8 +462,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_reduce_kernel(BwdParams p,
         }
     }
     const float sc = p.scale;
-    *(u32x2*)((uint16_t*)p.dk + e4) = u32x2{Op::pack2(sk[0] * sc, sk[1] * sc), Op::pack2(sk[2] * sc, sk[3] * sc)};
-    *(u32x2*)((uint16_t*)p.dv + e4) = u32x2{Op::pack2(sv[0], sv[1]), Op::pack2(sv[2], sv[3])};
+    const size_t o = ((size_t)slice * N + (size_t)kt * kKeyBlock + r) * D + j;
+    *(u32x2*)((uint16_t*)p.dk + o) = u32x2{Op::pack2(sk[0] * sc, sk[1] * sc), Op::pack2(sk[2] * sc, sk[3] * sc)};
+    *(u32x2*)((uint16_t*)p.dv + o) = u32x2{Op::pack2(sv[0], sv[1]), Op::pack2(sv[2], sv[3])};
 }
 
 // ---------------------------------------------------------------------------
@@ -614,21 +647,18 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
                        dim3(kBwdThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_kt = (int)((p.N + kKeyBlock - 1) / kKeyBlock);
-    // Many query heads per K/V head leave few dK/dV items, each long: split
-    // the heads over up to G/4 items (a power of two dividing G) until there
-    // are ~512 items. The fp32 partial sums of S splits take 8 S B*H_kv*N*D
-    // bytes, which fit dq's 2 G B*H_kv*N*D bytes while S <= G/4; dq is
-    // written last.
+    // Grouped-query heads make few, long dK/dV items (key tiles of unequal
+    // length under a causal mask): cut them into chunks of equal length,
+    // about two items per compute unit, when their partial sums fit dq's
+    // memory (bwd_chunks.h); dq is written last.
     BwdParams q = p;
-    q.splits = 1;
-    while (q.splits * 2 <= q.G / 4 && q.G % (q.splits * 2) == 0 &&
-           (int64_t)n_kt * q.BH_kv * q.splits < 512)
-        q.splits *= 2;
-    const dim3 grid_kv((unsigned)(n_kt * q.BH_kv * q.splits));
+    q.chunk = bwdplan::choose_chunk(q.N, q.G, q.BH_kv, CAUSAL, kDkdvItems);
+    const int64_t items = q.chunk > 0 ? bwdplan::plan_items(q.N, q.G, q.BH_kv, CAUSAL, q.chunk)
+                                      : (int64_t)bwdplan::n_key_tiles(q.N) * q.BH_kv;
+    const dim3 grid_kv((unsigned)items);
     bool two_groups = false;
     if constexpr (D == 64) {
-        if (q.G / q.splits > 1) {
+        if (q.G > 1) {
             hipLaunchKernelGGL((bwd_dkdv_kernel<IS_BF16, D, CAUSAL, 2>), grid_kv,
                                dim3(2 * kBwdThreads), 0, s, q);
             two_groups = true;
@@ -639,11 +669,11 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
                            s, q);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (q.splits > 1) {
-        const int64_t plane = (int64_t)q.BH_kv * q.N * D;
-        hipLaunchKernelGGL((bwd_kv_reduce_kernel<IS_BF16>),
-                           dim3((unsigned)((plane / 4 + kBwdThreads - 1) / kBwdThreads)),
-                           dim3(kBwdThreads), 0, s, q, plane);
+    if (q.chunk > 0) {
+        constexpr int WPT = kKeyBlock / (kBwdThreads / (D / 4));
+        const int64_t n_red = (int64_t)bwdplan::n_key_tiles(q.N) * WPT * q.BH_kv;
+        hipLaunchKernelGGL((bwd_kv_reduce_kernel<IS_BF16, D>), dim3((unsigned)n_red),
+                           dim3(kBwdThreads), 0, s, q, CAUSAL);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

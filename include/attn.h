@@ -115,8 +115,8 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* ls
  * k, v         DEVICE pointers, [B,H_kv,N,d] contiguous, `dtype`, 16-byte aligned.
  * lse          DEVICE pointer, [B,H,N] fp32: the forward's log-sum-exp.
  * dq           DEVICE pointer, [B,H,N,d] `dtype`, 16-byte aligned; written. For
- *              f16/bf16 with 8 or more query heads per K/V head its memory
- *              first holds the fp32 partial sums of dk and dv (before dq
+ *              f16/bf16 with 4 or more query heads per K/V head its memory
+ *              may first hold fp32 partial sums of dk and dv (before dq
  *              itself is written), so that the call allocates nothing.
  * dk, dv       DEVICE pointers, [B,H_kv,N,d] `dtype`, 16-byte aligned; written
  *              (not accumulated into).
@@ -132,8 +132,9 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* ls
  *              once (nearest even) from fp32; fp32 rounds nothing below fp32.
  * stream       hipStream_t (NULL = the null stream).
  *
- * Asynchronous: three kernels (four when f16/bf16 dk/dv work is split over
- * query-head groups) are enqueued on `stream` and the call returns;
+ * Asynchronous: three kernels (four when the f16/bf16 dk/dv work of
+ * grouped-query heads is cut into partial sums) are enqueued on `stream`
+ * and the call returns;
  * no host synchronisation, no device allocation, no atomics (results do not
  * depend on scheduling). Validation precedes any HIP call. Outputs must not
  * alias inputs or each other.
