@@ -256,21 +256,44 @@ def median_launch_ms(fn, n: int = 200) -> float:
     return ts[n // 2]
 
 
-def gfx_clock_under_load(fn, seconds: float = 2.0, ms_per_call: float = 0.1):
-    """Median GFX clock (MHz, from amdsmi) while launches of fn keep the GPU
-    busy (outside the timed region). amdsmi's readings trail the load by up
-    to about a second, so launches run without a break for `seconds` and
-    only readings from the second half count, each taken with ~25 ms of
-    launches queued and kept only while the stream still has work pending.
-    None where amdsmi is missing or refuses."""
+def device_state_under_load(fn, seconds: float = 2.0, ms_per_call: float = 0.1):
+    """GFX clock (MHz) and socket power (W), medians of amdsmi readings taken
+    while launches of fn keep the GPU busy (outside the timed region), the
+    board's power cap (W), and the share of that time the firmware held the
+    clock down for package power (its PPT violation counter over its tick
+    counter). amdsmi's readings trail the load by up to about a second, so
+    launches run without a break for `seconds` and only the second half
+    counts; each reading is taken with ~25 ms of launches queued and kept
+    only while the stream still has work pending. Read-only queries; each
+    field None where amdsmi is missing or refuses it."""
     import torch
+    state = {"gfx_clock_mhz": None, "socket_power_w": None, "power_cap_w": None,
+             "power_limited_frac": None}
     try:
         import amdsmi
         amdsmi.amdsmi_init()
         h = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
     except Exception:
-        return None
-    clocks = []
+        return state
+
+    def _try(f, *a):
+        try:
+            return f(*a)
+        except Exception:
+            return None
+
+    def _violation():
+        v = _try(amdsmi.amdsmi_get_violation_status, h)
+        if not isinstance(v, dict):
+            return None
+        ppt, ticks = v.get("acc_ppt_pwr"), v.get("acc_counter")
+        ok = isinstance(ppt, int) and isinstance(ticks, int)
+        return (ppt, ticks) if ok else None
+
+    cap = _try(amdsmi.amdsmi_get_power_cap_info, h)
+    if isinstance(cap, dict) and isinstance(cap.get("power_cap"), (int, float)) and cap["power_cap"] > 0:
+        state["power_cap_w"] = round(cap["power_cap"] / 1e6, 1)   # reported in microwatts
+    clocks, powers, v0 = [], [], None
     try:
         stream = torch.cuda.current_stream()
         per_sample = max(10, int(25.0 / max(ms_per_call, 1e-3)))
@@ -280,23 +303,30 @@ def gfx_clock_under_load(fn, seconds: float = 2.0, ms_per_call: float = 0.1):
                 fn()
             if time.perf_counter() - t0 < seconds / 2:
                 continue
-            info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
-            clk = info.get("clk") if isinstance(info, dict) else None
+            if v0 is None:
+                v0 = _violation() or (None,)
+            info = _try(amdsmi.amdsmi_get_clock_info, h, amdsmi.AmdSmiClkType.GFX)
+            pw = _try(amdsmi.amdsmi_get_power_info, h)
             busy = not stream.query()
+            clk = info.get("clk") if isinstance(info, dict) else None
+            sp = pw.get("socket_power") if isinstance(pw, dict) else None
             if busy and isinstance(clk, (int, float)) and clk > 0:
                 clocks.append(float(clk))
+            if busy and isinstance(sp, (int, float)) and sp > 0:
+                powers.append(float(sp))
+        v1 = _violation()
         torch.cuda.synchronize()
     except Exception:
-        return None
+        return state
     finally:
-        try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:
-            pass
-    if not clocks:
-        return None
-    clocks.sort()
-    return clocks[len(clocks) // 2]
+        _try(amdsmi.amdsmi_shut_down)
+    if clocks:
+        state["gfx_clock_mhz"] = sorted(clocks)[len(clocks) // 2]
+    if powers:
+        state["socket_power_w"] = sorted(powers)[len(powers) // 2]
+    if v0 and v0[0] is not None and v1 and v1[1] > v0[1]:
+        state["power_limited_frac"] = round((v1[0] - v0[0]) / (v1[1] - v0[1]), 3)
+    return state
 
 
 def _time_calls(fn, steps, warmup):
@@ -404,6 +434,9 @@ def main():
                          "K/V slices for the backward (default 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity gate")
+    ap.add_argument("--no-device-state", action="store_true",
+                    help="skip the ~2 s of extra launches that sample clock and power "
+                         "(for runs under a counter profiler, which serialises every launch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -482,7 +515,9 @@ def main():
     ms = start.elapsed_time(stop) / args.steps
     step_fn = lambda: ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out)   # noqa: E731
     ms_median = median_launch_ms(step_fn)
-    clock = gfx_clock_under_load(step_fn, ms_per_call=ms_median)
+    dev_state = (device_state_under_load(step_fn, ms_per_call=ms_median) if not args.no_device_state
+                 else dict.fromkeys(("gfx_clock_mhz", "socket_power_w", "power_cap_w",
+                                     "power_limited_frac")))
 
     flops = attention_flops(w.B, w.H, w.N, w.d, w.causal)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -512,7 +547,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": traffic},
         "ms_median_launch": round(ms_median, 5),
-        "gfx_clock_mhz_under_load": clock,
+        "gfx_clock_mhz_under_load": dev_state["gfx_clock_mhz"],
+        "socket_power_w_under_load": dev_state["socket_power_w"],
+        "power_cap_w": dev_state["power_cap_w"],
+        "power_limited_frac_under_load": dev_state["power_limited_frac"],
         "algorithmic_gb_s": round(abytes / (ms * 1e-3) / 1e9, 1),
         "exp_per_s": (w.B * w.H * w.N * w.N / (2 if w.causal else 1)) / (ms * 1e-3),
         "parity_o_max_abs_sampled": parity,
