@@ -54,7 +54,7 @@ def _capture(step):
 @pytest.mark.parametrize("dtype,d,H,H_kv", [
     (torch.bfloat16, 64, 4, 2),
     (torch.float32, 64, 4, 2),
-    # eight query heads per K/V head: split dK/dV partial sums and their
+    # eight query heads per K/V head: chunked dK/dV partial sums and their
     # reduction kernel inside the graph
     (torch.float16, 128, 8, 1),
 ], ids=["bf16-d64-gqa", "f32-d64-gqa", "f16-d128-split"])
