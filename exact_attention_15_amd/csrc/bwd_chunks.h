@@ -8,22 +8,23 @@
 // items become G times fewer and longer, and under a causal mask key tile kt
 // has (n_qs - 2 kt) G steps, so one round of items is as long as its first
 // key tile. Then every key tile's steps are cut into chunks of one length
-// L (the last chunk of a tile shorter), each chunk an item of its own that
-// writes fp32 partial sums of dK^T and dV^T; a reduction adds a tile's
-// chunks in chunk order (deterministic) into dK and dV.
+// L (the last chunk of a tile shorter), each chunk an item of its own. A
+// tile of more than one chunk has its chunks write fp32 partial sums of
+// dK^T and dV^T, which a reduction adds in chunk order (deterministic) into
+// dK and dV; a tile of one chunk is written directly, as without a plan.
 //
 // Partial sums live in dq's memory (2 G N D bytes per K/V slice for
-// f16/bf16, written by the last kernel only). Chunk c of key tile kt holds
-// rows(kt) partial rows (of 2 D floats: dK^T and dV^T) per K/V slice, so the
-// plan must satisfy  sum_kt n_chunks(kt) rows(kt) * 8 D <= 2 G N D, i.e.
-// sum_kt n_chunks(kt) rows(kt) <= G N / 4, which needs G >= 4.
+// f16/bf16, written by the last kernel only). Chunk c of a cut key tile kt
+// holds rows(kt) partial rows (of 2 D floats: dK^T and dV^T) per K/V slice,
+// so the plan must satisfy  sum over cut tiles of n_chunks(kt) rows(kt) * 8 D
+// <= 2 G N D, i.e. that sum of rows <= G N / 4.
 //
 // Layout of the partials (floats from the start of dq's memory), chunk c of
-// key tile kt, K/V slice s, key row r < rows(kt), column j < D:
+// cut key tile kt, K/V slice s, key row r < rows(kt), column j < D:
 //   block = (first(kt) kKeyBlock + c rows(kt)) BH_kv 2D + s rows(kt) 2D
 //   dK^T partial at block + r D + j, dV^T partial at block + (rows(kt) + r) D + j
-// with first(kt) the chunks of the earlier key tiles; as every key tile but
-// the last has kKeyBlock rows, the blocks tile the rows without overlap.
+// with first(kt) the chunks of the earlier cut key tiles; as every key tile
+// but the last has kKeyBlock rows, the blocks tile the rows without overlap.
 //
 // Plain constexpr functions: the kernels call them on device, the launcher on
 // the host, and a host test compiles this header with g++ alone.
@@ -54,6 +55,9 @@ constexpr int tile_rows(int64_t N, int kt) {
 
 constexpr int n_chunks(int steps, int chunk) { return (steps + chunk - 1) / chunk; }
 
+// Partial slots of a tile of nc chunks: none when it is written directly.
+constexpr int partial_slots(int nc) { return nc > 1 ? nc : 0; }
+
 // Item number w (over all K/V slices, key tile major, then chunk, then slice)
 // of a chunked plan.
 struct Item {
@@ -62,11 +66,12 @@ struct Item {
     int s0;      // first step
     int s1;      // one past the last step
     int64_t part_row;   // first(kt) kKeyBlock + c rows(kt): the block's row offset
+    bool partial;       // the tile is cut: write partial sums at part_row
     bool valid;  // w lies inside the plan
 };
 
 constexpr Item locate(int w, int64_t N, int G, int BH_kv, bool causal, int chunk) {
-    Item it{0, 0, 0, 0, 0, false};
+    Item it{0, 0, 0, 0, 0, false, false};
     const int n_qs = n_query_stages(N);
     const int n_kt = n_key_tiles(N);
     int rem = w / BH_kv;
@@ -80,20 +85,21 @@ constexpr Item locate(int w, int64_t N, int G, int BH_kv, bool causal, int chunk
             it.s0 = rem * chunk;
             it.s1 = it.s0 + chunk < steps ? it.s0 + chunk : steps;
             it.part_row = (int64_t)first * kKeyBlock + (int64_t)rem * tile_rows(N, kt);
+            it.partial = nc > 1;
             it.valid = true;
             return it;
         }
         rem -= nc;
-        first += nc;
+        first += partial_slots(nc);
     }
     return it;
 }
 
-// Chunks of the key tiles before kt (the reduction's view of the plan).
+// Partial slots of the key tiles before kt (the reduction's view of the plan).
 constexpr int first_chunk(int kt, int64_t N, int G, bool causal, int chunk) {
     const int n_qs = n_query_stages(N);
     int first = 0;
-    for (int k = 0; k < kt; ++k) first += n_chunks(kv_steps(G, n_qs, k, causal), chunk);
+    for (int k = 0; k < kt; ++k) first += partial_slots(n_chunks(kv_steps(G, n_qs, k, causal), chunk));
     return first;
 }
 
@@ -105,36 +111,40 @@ constexpr int64_t plan_items(int64_t N, int G, int BH_kv, bool causal, int chunk
     return n * BH_kv;
 }
 
-// Partial rows per K/V slice: sum_kt n_chunks(kt) rows(kt).
+// Partial rows per K/V slice: the sum over cut tiles of n_chunks(kt) rows(kt).
 constexpr int64_t plan_partial_rows(int64_t N, int G, bool causal, int chunk) {
     const int n_qs = n_query_stages(N);
     int64_t rows = 0;
     for (int kt = 0; kt < n_key_tiles(N); ++kt)
-        rows += (int64_t)n_chunks(kv_steps(G, n_qs, kt, causal), chunk) * tile_rows(N, kt);
+        rows += (int64_t)partial_slots(n_chunks(kv_steps(G, n_qs, kt, causal), chunk)) * tile_rows(N, kt);
     return rows;
 }
 
 // The chunk length for a call, or 0 for one item per key tile (partials not
-// used). Aims at about `target` items, the workgroups the device holds at
-// once; takes the shortest chunk whose partials fit dq's memory; keeps whole
-// key tiles unless chunks cut the longest item to at most 3/4 of its steps.
+// used): the shortest chunk whose items number at most `target` (the
+// workgroups the device holds at once: items past them would start a
+// second round, as long again) and whose partial sums fit dq's memory;
+// whole key tiles are kept unless chunks cut the longest item to at most
+// 3/4 of its steps.
 constexpr int choose_chunk(int64_t N, int G, int BH_kv, bool causal, int target) {
     const int n_qs = n_query_stages(N);
     const int longest = kv_steps(G, n_qs, 0, causal);
-    int64_t total = 0;
-    for (int kt = 0; kt < n_key_tiles(N); ++kt) total += kv_steps(G, n_qs, kt, causal);
-    total *= BH_kv;
-    const int64_t lo64 = (total + target - 1) / target;
     const int hi = (3 * (int64_t)longest) / 4;
-    if (lo64 > hi || hi < 1) return 0;
+    if (hi < 1) return 0;
     const int64_t cap_rows = (int64_t)G * N / 4;
-    if (plan_partial_rows(N, G, causal, hi) > cap_rows) return 0;
-    int lo = lo64 < 1 ? 1 : (int)lo64;
-    int top = hi;   // fits; find the smallest chunk in [lo, top] that fits
+    if (plan_items(N, G, BH_kv, causal, hi) > target || plan_partial_rows(N, G, causal, hi) > cap_rows)
+        return 0;
+    // Both conditions hold from some length on (longer chunks: fewer items,
+    // fewer cut tiles), so the shortest length meeting both is found by
+    // bisection over [1, hi].
+    int lo = 1, top = hi;
     while (lo < top) {
         const int mid = lo + (top - lo) / 2;
-        if (plan_partial_rows(N, G, causal, mid) <= cap_rows) top = mid;
-        else lo = mid + 1;
+        if (plan_items(N, G, BH_kv, causal, mid) <= target &&
+            plan_partial_rows(N, G, causal, mid) <= cap_rows)
+            top = mid;
+        else
+            lo = mid + 1;
     }
     return top;
 }

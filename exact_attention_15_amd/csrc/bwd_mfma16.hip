@@ -158,6 +158,7 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     const int n_qt = (N + kQStage - 1) / kQStage;
     int kt, kv_bh, s0, n_steps;
     int64_t part_row = 0;
+    bool partial = false;   // write partial sums (a cut key tile) instead of dK, dV
     if (p.chunk > 0) {
         const bwdplan::Item it = bwdplan::locate(w, N, p.G, p.BH_kv, CAUSAL, p.chunk);
         if (!it.valid) return;   // (the grid holds exactly the plan's items)
@@ -166,6 +167,7 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
         s0 = it.s0;
         n_steps = it.s1 - it.s0;
         part_row = it.part_row;
+        partial = it.partial;
     } else {
         kt = w / p.BH_kv;
         kv_bh = w - kt * p.BH_kv;
@@ -384,10 +386,10 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     }
 
     // dK = scale dK^T^T, dV = dV^T^T: lane l writes key `key`, entries
-    // d = 32 db + 8 i4 + 4g .. +3. A chunk item writes fp32 partial sums
-    // (not yet scaled) into dq's memory instead, in the layout of
-    // bwd_chunks.h; bwd_kv_reduce_kernel adds them up before dq is written.
-    if (p.chunk > 0) {
+    // d = 32 db + 8 i4 + 4g .. +3. A chunk of a cut key tile writes fp32
+    // partial sums (not yet scaled) into dq's memory instead, in the layout
+    // of bwd_chunks.h; bwd_kv_reduce_kernel adds them up before dq is written.
+    if (partial) {
         if (key < N) {
             const int rows = bwdplan::tile_rows(N, kt);
             float* blk = (float*)p.dq + ((size_t)part_row * p.BH_kv + (size_t)kv_bh * rows) * (2 * D);
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
 }
 
 // ---------------------------------------------------------------------------
-// (2b) Chunked dK/dV: dK = scale * the sum of a key tile's partial dK^T,
+// (2b) Chunked dK/dV: dK = scale * the sum of a cut key tile's partial dK^T,
 // dV = the sum of its partial dV^T, added in chunk order (deterministic).
 // Workgroup: RW rows of key tile kt of K/V slice `slice`, 4 columns a thread.
 template <bool IS_BF16, int D>
@@ -446,8 +448,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_reduce_kernel(BwdParams p,
     const int j = 4 * ((int)threadIdx.x % TPR);
     if (r >= rows) return;
     const int n_qt = bwdplan::n_query_stages(N);
-    const int first = bwdplan::first_chunk(kt, N, p.G, causal, p.chunk);
     const int nc = bwdplan::n_chunks(bwdplan::kv_steps(p.G, n_qt, kt, causal), p.chunk);
+    if (nc < 2) return;   // a key tile of one chunk wrote dK, dV itself
+    const int first = bwdplan::first_chunk(kt, N, p.G, causal, p.chunk);
     const float* part = (const float*)p.dq;
     f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
     for (int c = 0; c < nc; ++c) {

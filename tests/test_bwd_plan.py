@@ -1,7 +1,8 @@
 """Host logic of the 16-bit backward's dK/dV work plan (bwd_chunks.h,
 compiled here with g++ alone): the items cover every step of every key tile
-exactly once, chunk partial sums stay inside dq's memory without overlap,
-the reduction's view of the plan matches the items', and the chosen chunk
+exactly once, the chunks of cut key tiles keep their partial sums inside
+dq's memory without overlap, tiles of one chunk write directly, the
+reduction's view of the plan matches the items', and the chosen chunk
 length is the one its definition asks for (a brute-force search here)."""
 import os
 import subprocess
@@ -39,6 +40,12 @@ int main(int argc, char** argv) {
         if (it.s1 <= it.s0 || it.s1 - it.s0 > chunk) { printf("item %lld length\n", w); return 1; }
         std::vector<int>& sv = seen[it.kt * (size_t)BH_kv + it.slice];
         for (int s = it.s0; s < it.s1; ++s) sv[s] += 1;
+        const int nc = n_chunks(kv_steps(G, n_qs, it.kt, causal != 0), chunk);
+        if (it.partial != (nc > 1)) { printf("item %lld: direct/partial mismatch\n", w); return 1; }
+        if (!it.partial) {
+            if (it.s0 != 0 || it.s1 != (int)sv.size()) { printf("item %lld: direct item not a whole tile\n", w); return 1; }
+            continue;
+        }
         const int rows = tile_rows(N, it.kt);
         const long long blk = (it.part_row * BH_kv + (long long)it.slice * rows) * 2 * D;
         if (blk < 0 || blk + 2LL * rows * D > cap) { printf("item %lld partials out of dq\n", w); return 1; }
@@ -83,16 +90,18 @@ def _run(checker, N, G, BH_kv, causal, D=128, target=512):
 
 def _expected_chunk(N, G, BH_kv, causal, target=512):
     """The plan's definition, searched by brute force: the shortest chunk
-    length L >= total steps / target whose partial rows fit G*N/4 rows, kept
-    only if L cuts the longest key tile to <= 3/4 of its steps."""
+    length L whose items (over all K/V slices) number at most `target` and
+    whose partial rows (key tiles cut into two or more chunks only) fit
+    G*N/4 rows, kept only if L cuts the longest key tile to <= 3/4 of its
+    steps."""
     kb, qs = 128, 64
     n_qs = -(-N // qs)
     n_kt = -(-N // kb)
     steps = [G * (n_qs - 2 * kt if causal else n_qs) for kt in range(n_kt)]
     rows = [min(kb, N - kt * kb) for kt in range(n_kt)]
-    lo = max(1, -(-sum(steps) * BH_kv // target))
-    for L in range(lo, 3 * steps[0] // 4 + 1):
-        if sum(-(-w // L) * r for w, r in zip(steps, rows)) <= G * N // 4:
+    for L in range(1, 3 * steps[0] // 4 + 1):
+        items = BH_kv * sum(-(-w // L) for w in steps)
+        if items <= target and sum(-(-w // L) * r for w, r in zip(steps, rows) if w > L) <= G * N // 4:
             return L
     return 0
 
@@ -116,19 +125,28 @@ def test_plan_covers_steps_and_fits_dq(checker, N, G, BH_kv, causal):
 
 
 def test_plan_for_multi_query_d128():
-    """32 query heads on one K/V head, N = 8192, causal: items of ~290 steps
-    instead of whole key tiles (up to 4096 steps) and dq's memory used to
-    within a tile of its capacity."""
+    """32 query heads on one K/V head, N = 8192, causal: one round of at
+    most 512 items of ~270 steps instead of whole key tiles (up to 4096
+    steps), the partial sums within dq's memory."""
     n_kt, n_qs, G = 64, 128, 32
     L = _expected_chunk(8192, G, 1, True)
     steps = [G * (n_qs - 2 * kt) for kt in range(n_kt)]
     n_items = sum(-(-w // L) for w in steps)
-    assert 256 < L < 320 and 450 < n_items <= 512
-    assert n_items * 128 <= G * 8192 // 4
+    cut_rows = sum(-(-w // L) * 128 for w in steps if w > L)
+    assert 256 < L < 300 and 480 < n_items <= 512
+    assert cut_rows <= G * 8192 // 4
+
+
+def test_no_plan_when_items_fill_the_device(checker):
+    """Four query heads per K/V head, B*H_kv = 16, N = 4096, causal: the 512
+    whole key tiles already fill one round, and cutting any of them would
+    start a second round, so whole key tiles are kept."""
+    assert _run(checker, 4096, 4, 16, True) == (0, 512)
 
 
 def test_no_plan_without_grouped_heads(checker):
-    """One query head per K/V head: dq holds a quarter of the partials a
-    single chunk per key tile would need, so whole key tiles are kept."""
+    """One query head per K/V head: dq's memory holds partial sums for a
+    quarter of the key tiles, too few to cut the long ones in two, so whole
+    key tiles are kept."""
     for N in (64, 1000, 4096, 65536):
         assert _run(checker, N, 1, 4, True)[0] == 0
