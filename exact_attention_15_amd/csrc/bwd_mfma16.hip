@@ -62,7 +62,11 @@ static_assert(kKeyBlock == bwdplan::kKeyBlock && kQStage == bwdplan::kQStage,
               "the dK/dV item plan uses the kernel's tile sizes");
 constexpr int kQueryBlock = kBwdWaves * 32;   // query rows per dQ workgroup
 constexpr int kKStage = 64;                   // keys per LDS stage (dQ kernel)
-constexpr int kDkdvItems = 512;               // dK/dV workgroups resident at once (2 per CU)
+constexpr int kComputeUnits = 256;
+// dK/dV workgroups resident at once: __launch_bounds__ asks for two waves
+// per SIMD, so the one-group kernels (4 waves, <= 256 VGPRs) fit two per
+// CU; the two-group d = 64 kernel (8 waves, ~164 VGPRs) fits one.
+constexpr int dkdv_resident(int groups) { return kComputeUnits * (groups == 2 ? 1 : 2); }
 
 // 16-bit value to fp32.
 template <bool IS_BF16>
@@ -651,17 +655,18 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // Grouped-query heads make few, long dK/dV items (key tiles of unequal
-    // length under a causal mask): cut them into chunks of equal length,
-    // about two items per compute unit, when their partial sums fit dq's
-    // memory (bwd_chunks.h); dq is written last.
+    // length under a causal mask): cut them into chunks of equal length, no
+    // more items than the device holds at once, when their partial sums fit
+    // dq's memory (bwd_chunks.h); dq is written last.
     BwdParams q = p;
-    q.chunk = bwdplan::choose_chunk(q.N, q.G, q.BH_kv, CAUSAL, kDkdvItems);
+    const int groups = (D == 64 && q.G > 1) ? 2 : 1;   // the kernel launched below
+    q.chunk = bwdplan::choose_chunk(q.N, q.G, q.BH_kv, CAUSAL, dkdv_resident(groups));
     const int64_t items = q.chunk > 0 ? bwdplan::plan_items(q.N, q.G, q.BH_kv, CAUSAL, q.chunk)
                                       : (int64_t)bwdplan::n_key_tiles(q.N) * q.BH_kv;
     const dim3 grid_kv((unsigned)items);
     bool two_groups = false;
     if constexpr (D == 64) {
-        if (q.G > 1) {
+        if (groups == 2) {
             hipLaunchKernelGGL((bwd_dkdv_kernel<IS_BF16, D, CAUSAL, 2>), grid_kv,
                                dim3(2 * kBwdThreads), 0, s, q);
             two_groups = true;

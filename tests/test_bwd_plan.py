@@ -150,3 +150,12 @@ def test_no_plan_without_grouped_heads(checker):
     key tiles are kept."""
     for N in (64, 1000, 4096, 65536):
         assert _run(checker, N, 1, 4, True)[0] == 0
+
+
+def test_plan_for_the_two_group_kernel(checker):
+    """At d = 64 grouped-query items run in the two-group kernel, one per
+    compute unit (256 at once): its plan keeps to 256 items, so one round.
+    B*H_kv = 4, G = 16, N = 4096, causal."""
+    chunk, items = _run(checker, 4096, 16, 4, True, D=64, target=256)
+    assert chunk == _expected_chunk(4096, 16, 4, True, target=256) and items <= 256
+    assert chunk > _expected_chunk(4096, 16, 4, True, target=512) > 0
