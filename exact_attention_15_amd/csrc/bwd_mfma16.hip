@@ -22,8 +22,9 @@
 //     of scheduling: (1) D per row into the caller's fp32 `delta` buffer;
 //     (2) dK, dV: a workgroup owns 128 keys of one K/V head (32 per wave, its
 //     K and V fragments held in VGPRs) and streams every query tile that can
-//     see them, of every query head in the group, through LDS, two groups of
-//     waves taking alternate tiles; (3) dQ: a
+//     see them, of every query head in the group, through LDS (for
+//     grouped-query heads at d = 64, three groups of waves taking turns);
+//     (3) dQ: a
 //     workgroup owns 128 query rows (32 per wave, Q and dO held in VGPRs) and
 //     streams the K/V tiles. dQ is thus recomputed from S rather than summed
 //     across the dK/dV workgroups: one more product instead of a
@@ -63,10 +64,11 @@ static_assert(kKeyBlock == bwdplan::kKeyBlock && kQStage == bwdplan::kQStage,
 constexpr int kQueryBlock = kBwdWaves * 32;   // query rows per dQ workgroup
 constexpr int kKStage = 64;                   // keys per LDS stage (dQ kernel)
 constexpr int kComputeUnits = 256;
-// dK/dV workgroups resident at once: __launch_bounds__ asks for two waves
-// per SIMD, so the one-group kernels (4 waves, <= 256 VGPRs) fit two per
-// CU; the two-group d = 64 kernel (8 waves, ~164 VGPRs) fits one.
-constexpr int dkdv_resident(int groups) { return kComputeUnits * (groups == 2 ? 1 : 2); }
+constexpr int kGqaGroups = 3;                 // wave groups of a grouped-query d = 64 item
+// dK/dV workgroups resident at once: the one-group kernels (4 waves, asked
+// for two waves per SIMD, <= 256 VGPRs) fit two per CU; the three-group
+// d = 64 kernel (12 waves, asked for three per SIMD, <= 168 VGPRs) fits one.
+constexpr int dkdv_resident(int groups) { return kComputeUnits * (groups > 1 ? 1 : 2); }
 
 // 16-bit value to fp32.
 template <bool IS_BF16>
@@ -112,14 +114,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_delta_kernel(BwdParams p) {
 // that can see the keys, head-major) are dealt round-robin to GROUPS groups
 // of 4 waves, each with
 // its own LDS stage buffers and its own partial dK, dV for the same 128
-// keys; the partials are summed through LDS at the end. Two groups halve the
-// sequential length of an item at no extra traffic; they are used for
+// keys; the partials are summed through LDS at the end. Groups shorten the
+// sequential length of an item at no extra traffic; three are used for
 // grouped-query heads at d = 64, where an item spans G heads and the items
-// are G times fewer. (With one query head per item, two 4-wave workgroups
-// per CU keep more independent work in flight than one 8-wave workgroup;
-// at d = 128 the registers do not hold a second group's waves.)
+// are G times fewer (three waves per SIMD: the most the kernel's ~166
+// VGPRs allow). (With one query head per item, 4-wave workgroups, three
+// per CU, keep more independent work in flight; at d = 128 the registers
+// do not hold a second group's waves.)
 template <bool IS_BF16, int D, bool CAUSAL, int GROUPS>
-__global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads * GROUPS, GROUPS == 3 ? 3 : 2) void bwd_dkdv_kernel(BwdParams p) {
     using Op = Op16<IS_BF16>;
     using T = BTile<kQStage, D>;
     using Cp = BCopy<kQStage, D, kBwdWaves>;
@@ -130,7 +133,6 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     // loop the Q and dO space holds group 1's partial sums.
     static_assert(GROUPS == 1 || 4 * GROUPS * T::kBytes >= 2 * NDB * 16 * kBwdThreads * 4,
                   "reduction space");
-    static_assert(GROUPS <= 2, "one partial-sum hand-over");
     __shared__ __attribute__((aligned(1024))) char q_lds0[GROUPS * T::kBytes];
     __shared__ __attribute__((aligned(1024))) char q_lds1[GROUPS * T::kBytes];
     __shared__ __attribute__((aligned(1024))) char o_lds0[GROUPS * T::kBytes];   // dO
@@ -359,34 +361,40 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, 2) void bwd_dkdv_kernel(BwdPa
     }
     if (i < n_iter) step(i, P0{});
 
-    if constexpr (GROUPS == 2) {
-        // Group 1 hands its partial sums to group 0 through the Q and dO
-        // tiles (no copy is in flight and every wave is past its last read):
-        // element j of the thread's 2*NDB*16 sums at float j*256 + 64 wk +
-        // lane, spread over the four tile arrays (a quarter each).
+    if constexpr (GROUPS > 1) {
+        // Groups 1 .. GROUPS-1 in turn hand their partial sums to group 0
+        // through the Q and dO tiles (no copy is in flight and every wave is
+        // past its last read): element j of the thread's 2*NDB*16 sums at
+        // float j*256 + 64 wk + lane, spread over the four tile arrays.
         constexpr int kQuarter = GROUPS * T::kBytes / 4;   // floats per array
         LDS_AS float* const red4[4] = {(LDS_AS float*)q_lds0, (LDS_AS float*)q_lds1,
                                        (LDS_AS float*)o_lds0, (LDS_AS float*)o_lds1};
         auto red = [&](int idx) -> LDS_AS float& { return red4[idx / kQuarter][idx % kQuarter]; };
         const int slot = wk * 64 + lane;
-        if (grp == 1) {
+        for (int src = 1; src < GROUPS; ++src) {
+            if (grp == src) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    red(((2 * db + 0) * 16 + r) * kBwdThreads + slot) = dk[db][r];
-                    red(((2 * db + 1) * 16 + r) * kBwdThreads + slot) = dv[db][r];
-                }
-        }
-        __syncthreads();
-        if (grp == 1) return;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                dk[db][r] += red(((2 * db + 0) * 16 + r) * kBwdThreads + slot);
-                dv[db][r] += red(((2 * db + 1) * 16 + r) * kBwdThreads + slot);
+                    for (int r = 0; r < 16; ++r) {
+                        red(((2 * db + 0) * 16 + r) * kBwdThreads + slot) = dk[db][r];
+                        red(((2 * db + 1) * 16 + r) * kBwdThreads + slot) = dv[db][r];
+                    }
             }
+            __syncthreads();
+            if (grp == 0) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        dk[db][r] += red(((2 * db + 0) * 16 + r) * kBwdThreads + slot);
+                        dv[db][r] += red(((2 * db + 1) * 16 + r) * kBwdThreads + slot);
+                    }
+            }
+            // Group 0 has read one hand-over before the next is written.
+            if (src + 1 < GROUPS) __syncthreads();
+        }
+        if (grp != 0) return;
     }
 
     // dK = scale dK^T^T, dV = dV^T^T: lane l writes key `key`, entries
@@ -659,16 +667,16 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
     // more items than the device holds at once, when their partial sums fit
     // dq's memory (bwd_chunks.h); dq is written last.
     BwdParams q = p;
-    const int groups = (D == 64 && q.G > 1) ? 2 : 1;   // the kernel launched below
+    const int groups = (D == 64 && q.G > 1) ? kGqaGroups : 1;   // the kernel launched below
     q.chunk = bwdplan::choose_chunk(q.N, q.G, q.BH_kv, CAUSAL, dkdv_resident(groups));
     const int64_t items = q.chunk > 0 ? bwdplan::plan_items(q.N, q.G, q.BH_kv, CAUSAL, q.chunk)
                                       : (int64_t)bwdplan::n_key_tiles(q.N) * q.BH_kv;
     const dim3 grid_kv((unsigned)items);
     bool two_groups = false;
     if constexpr (D == 64) {
-        if (groups == 2) {
-            hipLaunchKernelGGL((bwd_dkdv_kernel<IS_BF16, D, CAUSAL, 2>), grid_kv,
-                               dim3(2 * kBwdThreads), 0, s, q);
+        if (groups == kGqaGroups) {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<IS_BF16, D, CAUSAL, kGqaGroups>), grid_kv,
+                               dim3(kGqaGroups * kBwdThreads), 0, s, q);
             two_groups = true;
         }
     }

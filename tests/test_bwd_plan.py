@@ -153,7 +153,7 @@ def test_no_plan_without_grouped_heads(checker):
 
 
 def test_plan_for_the_two_group_kernel(checker):
-    """At d = 64 grouped-query items run in the two-group kernel, one per
+    """At d = 64 grouped-query items run in the three-group kernel, one per
     compute unit (256 at once): its plan keeps to 256 items, so one round.
     B*H_kv = 4, G = 16, N = 4096, causal."""
     chunk, items = _run(checker, 4096, 16, 4, True, D=64, target=256)

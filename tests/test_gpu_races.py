@@ -90,7 +90,7 @@ def test_forward_two_query_blocks_matches_probe_build(libs, dtype):
 
 
 @pytest.mark.parametrize("dtype,d,H,H_kv", [
-    (torch.bfloat16, 64, 4, 2),    # two wave groups per dK/dV item
+    (torch.bfloat16, 64, 4, 2),    # three wave groups per dK/dV item
     (torch.bfloat16, 64, 4, 4),
     (torch.float16, 128, 8, 1),    # split dK/dV partial sums and their reduction
     (torch.float32, 64, 4, 2),     # four wave groups, paired tiles
