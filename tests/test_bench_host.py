@@ -42,3 +42,15 @@ def test_traffic_is_tied_to_the_kernel_sources():
     else:
         assert got is None
     assert bench.measured_traffic("no_such_workload") is None
+
+
+def test_device_state_degrades_to_nulls_without_a_device():
+    """The clock / power sampler is outside the timed region and must never
+    fail a bench run: without a GPU (or without amdsmi) every field is None,
+    and the function returns without calling the step."""
+    calls = []
+    state = bench.device_state_under_load(lambda: calls.append(1), seconds=0.05)
+    assert set(state) == {"gfx_clock_mhz", "socket_power_w", "power_cap_w", "power_limited_frac"}
+    import torch
+    if not torch.cuda.is_available():
+        assert all(v is None for v in state.values()) and not calls
