@@ -115,9 +115,9 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* ls
  * k, v         DEVICE pointers, [B,H_kv,N,d] contiguous, `dtype`, 16-byte aligned.
  * lse          DEVICE pointer, [B,H,N] fp32: the forward's log-sum-exp.
  * dq           DEVICE pointer, [B,H,N,d] `dtype`, 16-byte aligned; written. For
- *              f16/bf16 with 4 or more query heads per K/V head its memory
- *              may first hold fp32 partial sums of dk and dv (before dq
- *              itself is written), so that the call allocates nothing.
+ *              f16/bf16 with grouped-query heads (H_kv < H) its memory may
+ *              first hold fp32 partial sums of dk and dv (before dq itself
+ *              is written), so that the call allocates nothing.
  * dk, dv       DEVICE pointers, [B,H_kv,N,d] `dtype`, 16-byte aligned; written
  *              (not accumulated into).
  * delta        DEVICE pointer, [B,H,N] fp32, 4-byte aligned; written with D_i

@@ -82,10 +82,11 @@ def _bwd_and_check(ea, oracle_lib, q, k, v, dout, causal, scale, what):
 
 SWEEP = [(1, 2, 2), (2, 4, 1), (17, 2, 2), (64, 4, 2), (65, 2, 2), (127, 6, 3), (128, 2, 2),
          (129, 4, 4), (200, 4, 1), (257, 2, 2),
-         # 8 or 16 query heads per K/V head: the dK/dV work of a key tile is
-         # cut into chunks whose partial sums are reduced afterwards (also a
-         # one-row and a 33-row key tile)
-         (65, 16, 1), (130, 8, 1), (257, 16, 2), (1, 8, 1), (33, 16, 2)]
+         # 2, 8 or 16 query heads per K/V head: the dK/dV work of a key tile
+         # is cut into chunks whose partial sums are reduced afterwards (also
+         # a one-row and a 33-row key tile; at G = 2 only the two longest
+         # causal key tiles are cut)
+         (65, 16, 1), (130, 8, 1), (257, 16, 2), (1, 8, 1), (33, 16, 2), (1024, 4, 2)]
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32],
