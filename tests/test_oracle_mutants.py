@@ -50,6 +50,24 @@ MUTANTS = [
      "dv[c] += pj * grow[c];", "dv[c] += pj * qrow[c];"),
     ("backward: dQ without the scale",
      "        dq[c] *= w->scale;\n    if (w->eq) {", "        dq[c] *= 1.0;\n    if (w->eq) {"),
+    # The backward error scales set the backward parity tolerance; an
+    # inflated one would loosen it silently.
+    ("backward error scale: eq doubled",
+     "eq[c] *= w->scale;", "eq[c] *= 2.0 * w->scale;"),
+    ("backward error scale: ek doubled",
+     "const double b = w->scale * wt[j];", "const double b = 2.0 * w->scale * wt[j];"),
+    ("backward error scale: ev doubled",
+     "ev[c] += pj * ga[c];", "ev[c] += 2.0 * pj * ga[c];"),
+    ("backward error scale: zq doubled",
+     "zq[c] *= w->scale;", "zq[c] *= 2.0 * w->scale;"),
+    ("backward error scale: zk with a doubled rounding term",
+     "const double z = w->scale * (1.0 + pj * gs);", "const double z = w->scale * (2.0 + pj * gs);"),
+    ("backward error scale: o's rounding counted twice in w",
+     "wt[j] = fabs(ds[j]) + p[j] * A;", "wt[j] = fabs(ds[j]) + 2.0 * p[j] * A;"),
+    ("backward error scale: eq over signed k",
+     "eq[c] += wt[j] * w->ka[j * d + c];", "eq[c] += wt[j] * kd[j * d + c];"),
+    ("backward error scale: o's rounding dropped from w",
+     "A += fabs(grow[c] * orow[c]);", "A += 0.0;"),
 ]
 
 

@@ -543,6 +543,115 @@ def test_bwd_identities(orc, causal):
     assert np.all(zk >= 0) and np.all(zq >= 0)
 
 
+def _bwd_model(q, k, v, dout, causal, scale):
+    """The backward pass written out from the chain rule in numpy fp64, with
+    K/V heads expanded to one per query head: P, O, dP = dO V^T, D and dS."""
+    G = q.shape[1] // k.shape[1]
+    Q, K, V, dO = (_f64(t) for t in (q, k, v, dout))
+    K, V = np.repeat(K, G, axis=1), np.repeat(V, G, axis=1)
+    s = float(scale) * Q @ np.swapaxes(K, -1, -2)
+    vis = np.ones(s.shape[-2:], dtype=bool)
+    if causal:
+        vis = np.tril(vis)
+    s = np.where(vis, s, -np.inf)
+    P = np.exp(s - s.max(axis=-1, keepdims=True))
+    P /= P.sum(axis=-1, keepdims=True)
+    O = P @ V
+    dP = dO @ np.swapaxes(V, -1, -2)
+    D = (dO * O).sum(axis=-1)
+    return Q, K, dO, P, O, dP, D, vis, G
+
+
+def _bwd_grads(Q, K, dO, P, dS, scale, G):
+    """dq, dk, dv from P and dS; dk, dv summed over each K/V head's query heads."""
+    B, H, N, d = Q.shape
+    dq = float(scale) * dS @ K
+    dk = float(scale) * np.swapaxes(dS, -1, -2) @ Q
+    dv = np.swapaxes(P, -1, -2) @ dO
+    fold = lambda x: x.reshape(B, H // G, G, N, d).sum(axis=2)   # noqa: E731
+    return dq, fold(dk), fold(dv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_error_scales_are_attained(orc, causal):
+    """The error scales are the exact worst case of their rounding model, not
+    just an upper bound. The model: p, dS and O are each rounded once, with a
+    relative error of at most u (the e scales) or an absolute one of at most
+    s/2 (the z scales), and the rounded O enters dS through D. With Q, K and
+    dO non-negative every gradient element is moved furthest by one and the
+    same perturbation (dS and p pushed up, O pushed against the sign of
+    dO * O), so the perturbed chain rule, recomputed from scratch, must move
+    dq, dk, dv by exactly u e (and s/2 z): an inflated, deflated or
+    mis-assembled scale fails, where the bound e >= |grad| alone would let an
+    inflated scale pass."""
+    B, H, H_kv, N, d = 1, 4, 2, 13, 8
+    q, k, v, dout = _grads_inputs(B, H, H_kv, N, d, torch.float32, seed=120)
+    q, k, dout = q.abs(), k.abs(), dout.abs()
+    scale = 0.375
+    dq, dk, dv, eq, ek, ev, zq, zk, zv = orc.attn_bwd_ref(q, k, v, dout, causal, scale,
+                                                          error_scales=True)
+    Q, K, dO, P, O, dP, D, vis, G = _bwd_model(q, k, v, dout, causal, scale)
+    g0 = _bwd_grads(Q, K, dO, P, P * (dP - D[..., None]), scale, G)
+    for got, ref in zip((dq, dk, dv), g0):
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+    u = 2.0 ** -20
+    dS = P * (dP - D[..., None])
+    o_t = O * (1 - u * np.sign(dO * O))                      # D moves by -u sum |dO o|
+    dS_t = P * (dP - (dO * o_t).sum(axis=-1)[..., None]) * (1 + u * np.sign(dS))
+    g_rel = _bwd_grads(Q, K, dO, P * (1 + u), dS_t, scale, G)
+    for moved, base, e in zip(g_rel, g0, (eq, ek, ev)):
+        np.testing.assert_allclose((moved - base) / u, e, rtol=2e-5, atol=1e-12)
+
+    h = 2.0 ** -20                                           # s / 2
+    o_a = O - h * np.sign(dO)                                # D moves by -h sum |dO|
+    dS_a = P * (dP - (dO * o_a).sum(axis=-1)[..., None]) + h * vis
+    g_abs = _bwd_grads(Q, K, dO, P + h * vis, dS_a, scale, G)
+    for moved, base, z in zip(g_abs, g0, (zq, zk, zv)):
+        np.testing.assert_allclose((moved - base) / h, z, rtol=2e-5, atol=1e-12)
+    # dO >= 0: the value gradient's relative scale is the gradient itself
+    np.testing.assert_allclose(ev, dv, rtol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_error_scales_bound_signed_worst_case(orc, causal):
+    """With signed inputs the scales still bound the worst case of the model,
+    found here element by element: for each column c of dq (and of dk) the
+    perturbation of dS takes the sign of dS_ij k_jc (q_ic), and O's moves D
+    in the direction that adds to it; the perturbed chain rule is recomputed
+    per column. The relative part of that worst case, sum_j |dS_ij k_jc|, is
+    attained exactly, so a scale that dropped an absolute value (or a term)
+    falls below it."""
+    B, H, H_kv, N, d = 1, 2, 1, 11, 6
+    q, k, v, dout = _grads_inputs(B, H, H_kv, N, d, torch.float32, seed=121)
+    scale = 0.5
+    _, _, _, eq, ek, _, _, _, _ = orc.attn_bwd_ref(q, k, v, dout, causal, scale,
+                                                   error_scales=True)
+    Q, K, dO, P, O, dP, D, vis, G = _bwd_model(q, k, v, dout, causal, scale)
+    dS = P * (dP - D[..., None])
+    u = 2.0 ** -20
+    base = _bwd_grads(Q, K, dO, P, dS, scale, G)
+    for c in range(d):
+        # dq column c: sign of dS_ij k_jc; D's move adds sign(sum_j p_ij k_jc)
+        kc = K[..., c]                                        # [B, H, N] (expanded heads)
+        dSk = dS * kc[..., None, :]
+        turn = np.sign((P * kc[..., None, :]).sum(axis=-1))   # [B, H, N] per query row
+        o_t = O * (1 - u * turn[..., None] * np.sign(dO * O))
+        Dt = (dO * o_t).sum(axis=-1)
+        dS_t = P * (dP - Dt[..., None]) * (1 + u * np.sign(dSk))
+        worst = np.abs(_bwd_grads(Q, K, dO, P, dS_t, scale, G)[0][..., c] - base[0][..., c]) / u
+        ds_part = float(scale) * np.abs(dSk).sum(axis=-1)
+        assert np.all(worst <= eq[..., c] * (1 + 1e-5) + 1e-12)
+        assert np.all(worst >= ds_part * (1 - 1e-5) - 1e-12)
+        assert np.all(eq[..., c] >= ds_part * (1 - 1e-9))
+        # dk column c: sign of dS_ij q_ic, summed over the group's query heads
+        qc = Q[..., c]                                        # [B, H, N]
+        dSq = dS * qc[..., :, None]
+        dS_t = dS * (1 + u * np.sign(dSq))
+        worst_k = np.abs(_bwd_grads(Q, K, dO, P, dS_t, scale, G)[1][..., c] - base[1][..., c]) / u
+        assert np.all(ek[..., c] >= worst_k * (1 - 1e-5) - 1e-12)
+
+
 def test_bwd_special_cases(orc):
     # N = 1: o = v, so dv = dout and dq = dk = 0
     q, k, v, dout = _grads_inputs(1, 2, 2, 1, 8, torch.float32, seed=80)
