@@ -149,6 +149,38 @@ constexpr int choose_chunk(int64_t N, int G, int BH_kv, bool causal, int target)
     return top;
 }
 
+// Wave groups of a dK/dV item and how many such workgroups a compute unit
+// holds. The one-group kernel is 4 waves (one per SIMD); its d = 64 build
+// takes 156-166 VGPRs, so three waves fit a SIMD's 512 registers and three
+// workgroups a compute unit, its d = 128 build takes 256 (two). The
+// three-group kernel (12 waves, d = 64 only) fits once per compute unit.
+// tests/test_build_flags.py checks these counts against the compiler's.
+constexpr int kGroupedWaveGroups = 3;
+constexpr int one_group_per_cu(int D) { return D == 64 ? 3 : 2; }
+constexpr int dkdv_resident(int D, int groups, int compute_units) {
+    return compute_units * (groups > 1 ? 1 : one_group_per_cu(D));
+}
+
+// Wave groups per dK/dV item. Grouped-query items at d = 64 take three. So
+// do multi-head non-causal ones at d = 64 when the last round of equal
+// items would leave the one-group kernel's slots mostly idle: the
+// three-group kernel gives ~0.70 of the one-group throughput per compute
+// unit (fp16 B1 H8 N16384: 1024 items, 2.04 ms with one group in two
+// rounds of 768, 1.94 ms with three in four rounds of 256) but its rounds
+// come out fuller. Causal items differ in length and, longest first, fill
+// their rounds (bf16 causal B4 H16 N4096: one group 0.48 ms, three 0.54 ms).
+constexpr int dkdv_groups(int D, bool causal, int G, int64_t N, int BH_kv, int compute_units) {
+    if (D != 64) return 1;
+    if (G > 1) return kGroupedWaveGroups;
+    if (causal) return 1;
+    const int64_t items = (int64_t)n_key_tiles(N) * BH_kv;
+    const int64_t slots1 = dkdv_resident(D, 1, compute_units);
+    const int64_t slots3 = dkdv_resident(D, kGroupedWaveGroups, compute_units);
+    const double fill1 = (double)items / (double)(((items + slots1 - 1) / slots1) * slots1);
+    const double fill3 = (double)items / (double)(((items + slots3 - 1) / slots3) * slots3);
+    return 0.70 * fill3 > 1.02 * fill1 ? kGroupedWaveGroups : 1;
+}
+
 }  // namespace bwdplan
 }  // namespace attn
 

@@ -64,33 +64,7 @@ static_assert(kKeyBlock == bwdplan::kKeyBlock && kQStage == bwdplan::kQStage,
 constexpr int kQueryBlock = kBwdWaves * 32;   // query rows per dQ workgroup
 constexpr int kKStage = 64;                   // keys per LDS stage (dQ kernel)
 constexpr int kComputeUnits = 256;
-constexpr int kGqaGroups = 3;                 // wave groups of a grouped-query d = 64 item
-// dK/dV workgroups resident at once: the one-group kernels (4 waves, asked
-// for two waves per SIMD, <= 256 VGPRs) fit two per CU; the three-group
-// d = 64 kernel (12 waves, asked for three per SIMD, <= 168 VGPRs) fits one.
-constexpr int dkdv_resident(int groups) { return kComputeUnits * (groups > 1 ? 1 : 2); }
-
-// Wave groups per dK/dV item. Grouped-query items at d = 64 take three. So
-// do multi-head non-causal ones at d = 64 when the last round of equal
-// items would leave the one-group kernel's slots (three 4-wave workgroups
-// per CU at d = 64) mostly idle: the three-group kernel gives ~0.70 of the
-// one-group throughput per CU (fp16 B1 H8 N16384: 1024 items, 2.04 ms with
-// one group in two rounds of 768, 1.94 ms with three in four rounds of
-// 256) but holds 256 items, so its rounds come out fuller. Causal items
-// differ in length and, longest first, fill their rounds (bf16 causal B4
-// H16 N4096: one group 0.48 ms, three 0.54 ms).
-template <int D, bool CAUSAL>
-int dkdv_groups(const BwdParams& q) {
-    if (D != 64) return 1;
-    if (q.G > 1) return kGqaGroups;
-    if (CAUSAL) return 1;
-    const int64_t items = (int64_t)bwdplan::n_key_tiles(q.N) * q.BH_kv;
-    const int64_t slots1 = 3 * (int64_t)kComputeUnits, slots3 = kComputeUnits;
-    const double fill1 = (double)items / (double)(((items + slots1 - 1) / slots1) * slots1);
-    const double fill3 = (double)items / (double)(((items + slots3 - 1) / slots3) * slots3);
-    return 0.70 * fill3 > 1.02 * fill1 ? kGqaGroups : 1;
-}
-
+constexpr int kGqaGroups = bwdplan::kGroupedWaveGroups;   // wave groups of a grouped-query d = 64 item
 // 16-bit value to fp32.
 template <bool IS_BF16>
 __device__ __forceinline__ float lo16(uint32_t w) {
@@ -688,8 +662,10 @@ hipError_t launch(const BwdParams& p, hipStream_t s) {
     // more items than the device holds at once, when their partial sums fit
     // dq's memory (bwd_chunks.h); dq is written last.
     BwdParams q = p;
-    const int groups = dkdv_groups<D, CAUSAL>(q);   // the kernel launched below
-    q.chunk = bwdplan::choose_chunk(q.N, q.G, q.BH_kv, CAUSAL, dkdv_resident(groups));
+    // the kernel launched below
+    const int groups = bwdplan::dkdv_groups(D, CAUSAL, q.G, q.N, q.BH_kv, kComputeUnits);
+    q.chunk = bwdplan::choose_chunk(q.N, q.G, q.BH_kv, CAUSAL,
+                                    bwdplan::dkdv_resident(D, groups, kComputeUnits));
     const int64_t items = q.chunk > 0 ? bwdplan::plan_items(q.N, q.G, q.BH_kv, CAUSAL, q.chunk)
                                       : (int64_t)bwdplan::n_key_tiles(q.N) * q.BH_kv;
     const dim3 grid_kv((unsigned)items);

@@ -37,7 +37,13 @@ def _compile(src):
         m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
         if m and name:
             scratch[name] = int(m.group(1))
+        m = re.search(r"\b([VA])GPRs: (\d+)", line)
+        if m and name:
+            REGS.setdefault(name, {})[m.group(1)] = int(m.group(2))
     return r.stdout, scratch
+
+
+REGS = {}   # kernel -> {"V": VGPRs, "A": AGPRs}, filled by _compile
 
 
 @pytest.fixture(scope="module")
@@ -68,3 +74,23 @@ def test_no_register_spills_beyond_the_known_one(compiled):
         if v > allowed:
             over[k] = v
     assert not over, over
+
+
+def _waves_per_simd(regs):
+    """Waves of one kernel a SIMD holds: 512 registers per lane, VGPRs and
+    AGPRs together, allocated in granules of 8."""
+    used = regs.get("V", 0) + regs.get("A", 0)
+    return 512 // (-(-used // 8) * 8)
+
+
+def test_dkdv_residency_matches_the_plan(compiled):
+    """The backward's work plan (bwd_chunks.h, one_group_per_cu) counts
+    three one-group dK/dV workgroups per compute unit at d = 64 and two at
+    d = 128; the compiler's register counts must give exactly that."""
+    seen = {64: [], 128: []}
+    for k, regs in REGS.items():
+        m = re.search(r"bwd_dkdv_kernelILb[01]ELi(64|128)ELb[01]ELi1E", k)
+        if m:
+            seen[int(m.group(1))].append(_waves_per_simd(regs))
+    assert len(seen[64]) == 4 and len(seen[128]) == 4, seen
+    assert set(seen[64]) == {3} and set(seen[128]) == {2}, seen

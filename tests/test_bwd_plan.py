@@ -159,3 +159,53 @@ def test_plan_for_the_two_group_kernel(checker):
     chunk, items = _run(checker, 4096, 16, 4, True, D=64, target=256)
     assert chunk == _expected_chunk(4096, 16, 4, True, target=256) and items <= 256
     assert chunk > _expected_chunk(4096, 16, 4, True, target=512) > 0
+
+
+GROUPS_CHECKER = r"""
+#include <cstdio>
+#include <cstdlib>
+#include "bwd_chunks.h"
+using namespace attn::bwdplan;
+int main(int argc, char** argv) {
+    const int D = atoi(argv[1]), causal = atoi(argv[2]), G = atoi(argv[3]);
+    const long long N = atoll(argv[4]);
+    const int BH_kv = atoi(argv[5]);
+    const int groups = dkdv_groups(D, causal != 0, G, N, BH_kv, 256);
+    printf("%d %d\n", groups, dkdv_resident(D, groups, 256));
+    return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def groups_checker(tmp_path_factory):
+    d = tmp_path_factory.mktemp("groups")
+    src = d / "groups.cpp"
+    src.write_text(GROUPS_CHECKER)
+    exe = d / "groups"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", build.CSRC, str(src), "-o", str(exe)],
+                   check=True)
+    return str(exe)
+
+
+@pytest.mark.parametrize("D,causal,G,N,BH_kv,want", [
+    # non-causal multi-head d = 64: one group while its rounds of 768 fill
+    (64, 0, 1, 1280, 64, (1, 768)),      # B1 H64 N1280: 640 items
+    (64, 0, 1, 8192, 64, (1, 768)),      # B4 H16 N8192: 4096 items
+    (64, 0, 1, 2048, 48, (1, 768)),      # 768 items, one full round
+    (64, 0, 1, 16384, 8, (3, 256)),      # 1024 items: second round of 768 mostly empty
+    (64, 0, 1, 300, 12, (3, 256)),       # 36 items
+    (64, 0, 1, 4096, 8, (3, 256)),       # 256 items
+    # causal and grouped-query items, and d = 128
+    (64, 1, 1, 4096, 64, (1, 768)),
+    (64, 1, 4, 4096, 16, (3, 256)),
+    (64, 0, 2, 1280, 32, (3, 256)),
+    (128, 0, 1, 16384, 8, (1, 512)),
+    (128, 1, 32, 8192, 1, (1, 512)),
+])
+def test_dkdv_group_choice(groups_checker, D, causal, G, N, BH_kv, want):
+    """Which dK/dV kernel a call runs (the one-group or the three-group one)
+    and the resident-workgroup count its plan targets."""
+    r = subprocess.run([groups_checker, str(D), str(causal), str(G), str(N), str(BH_kv)],
+                       check=True, capture_output=True, text=True)
+    assert tuple(int(x) for x in r.stdout.split()) == want

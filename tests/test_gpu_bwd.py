@@ -121,6 +121,18 @@ def test_bwd_scale_and_values(ea, oracle_lib):
     _bwd_and_check(ea, oracle_lib, q, k, v, dout, True, 0.3, "scale 0.3, values x2")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_bwd_one_group_noncausal_mha(ea, oracle_lib, dtype):
+    """Non-causal multi-head d = 64 with 640 dK/dV items (B1 H64 N1280):
+    enough to fill rounds of the one-group dK/dV kernel, which the launcher
+    therefore picks over the three-group one (the choice is pinned on the
+    host in tests/test_bwd_plan.py); every element."""
+    q, k, v = make_qkv(1, 64, 1280, 64, dtype, seed=9700)
+    dout = make_dout(1, 64, 1280, 64, dtype, seed=9700)
+    _bwd_and_check(ea, oracle_lib, q, k, v, dout, False, ea.default_scale(64),
+                   f"one-group dK/dV B1 H64 N1280 {dtype}")
+
+
 FULL = ["c3_bf16_causal", "g1_bf16_causal_gqa4", "c4_bf16_d128_causal", "c2_f32_causal"]
 
 

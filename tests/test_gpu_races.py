@@ -115,3 +115,16 @@ def test_unfused_matches_probe_build(libs, dtype, d):
     q, k, v = (t.cuda() for t in make_qkv(1, 3, 333, d, dtype, seed=7500 + d))
     _same(_unfused(ea, lib, q, k, v, True), _unfused(ea, probe, q, k, v, True),
           f"unfused {dtype} d={d}")
+
+
+def test_backward_one_group_matches_probe_build(libs):
+    """Non-causal multi-head d = 64 with 640 dK/dV items (B1 H64 N1280), which
+    runs the one-group dK/dV kernel."""
+    ea, lib, probe = libs
+    n = 1280
+    q, k, v = (t.cuda() for t in make_qkv(1, 64, n, 64, torch.bfloat16, seed=7460))
+    dout = make_dout(1, 64, n, 64, torch.bfloat16, seed=7460).cuda()
+    o, lse = _fwd(ea, lib, q, k, v, False)
+    _same(_bwd(ea, lib, q, k, v, o, lse, dout, False),
+          _bwd(ea, probe, q, k, v, o, lse, dout, False),
+          "backward one-group bf16 d=64 H=64 N=1280")
