@@ -16,7 +16,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
-ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EALIGN, ATTN_EHIP = 0, -1, -2, -3, -4
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EALIGN, ATTN_EHIP, ATTN_ETOOBIG = 0, -1, -2, -3, -4, -5
+BWD_NOALLOC_MAX_ROWS = 4 * 1024 * 1024   # ATTN_BWD_NOALLOC_MAX_ROWS
 
 _lib = None
 
@@ -62,6 +63,9 @@ def _configure(lib):
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                              ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                     ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
     lib.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                      ctypes.c_int, ctypes.c_float, ctypes.c_int, vp]
     lib.attn_fwd_unfused.restype = ctypes.c_int
@@ -212,6 +216,13 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     return dq, dk, dv
 
 
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, causal, scale, dtype,
+                     stream) -> int:
+    """Raw C-ABI call of the allocation-free backward (no delta argument)."""
+    return load_library().attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d,
+                                           int(causal), float(scale), int(dtype), stream)
+
+
 def attn_fwd_unfused(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, causal, scale,
                      dtype, stream) -> int:
     """Raw C-ABI call of the unfused three-kernel forward."""
@@ -257,5 +268,5 @@ def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, works
     return o, lse
 
 
-__all__ = ["fwd", "bwd", "fwd_unfused", "attn_fwd_unfused", "unfused_workspace_bytes", "attn_bwd", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
+__all__ = ["fwd", "bwd", "fwd_unfused", "attn_fwd_unfused", "unfused_workspace_bytes", "attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
            "dtype_code", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -2,10 +2,13 @@
 // (dtype, head dim, causal) and launch on the caller's stream.
 //
 // Validation happens before any HIP call, so an error code means nothing was
-// enqueued. The library keeps no state and allocates nothing.
+// enqueued. The library allocates nothing; its one piece of state is the
+// per-device address of attn_bwd_noalloc's static row-statistic array.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "attn_internal.h"
@@ -30,6 +33,20 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
     const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u;
     if (mis != 0 || ((uintptr_t)lse & 3u) != 0) return ATTN_EALIGN;
     return ATTN_OK;
+}
+
+// attn_bwd's checks other than those of `delta`.
+int validate_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, const void* dq, const void* dk, const void* dv, int64_t B,
+                 int64_t H, int64_t H_kv, int64_t N, int64_t d, int causal, float scale,
+                 int dtype) {
+    const int rc = validate(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (!dout || !dq || !dk || !dv) return ATTN_EINVAL;
+    // The row-statistic kernel covers 16 rows or more per workgroup.
+    if (B * H * N / 16 >= (int64_t)INT32_MAX) return ATTN_EINVAL;
+    const uintptr_t mis = ((uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u;
+    return mis != 0 ? ATTN_EALIGN : ATTN_OK;
 }
 
 }  // namespace
@@ -69,13 +86,11 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
                         float* delta, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
                         int causal, float scale, int dtype, void* stream) {
-    int rc = validate(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, dtype);
+    const int rc = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, causal,
+                                scale, dtype);
     if (rc != ATTN_OK) return rc;
-    if (!dout || !dq || !dk || !dv || !delta) return ATTN_EINVAL;
-    // The row-statistic kernel covers 16 rows or more per workgroup.
-    if (B * H * N / 16 >= (int64_t)INT32_MAX) return ATTN_EINVAL;
-    const uintptr_t mis = ((uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u;
-    if (mis != 0 || ((uintptr_t)delta & 3u) != 0) return ATTN_EALIGN;
+    if (!delta) return ATTN_EINVAL;
+    if (((uintptr_t)delta & 3u) != 0) return ATTN_EALIGN;
 
     attn::BwdParams p;
     p.q = q;
@@ -103,6 +118,63 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
             ? attn::launch_bwd32(p, (int)d, causal != 0, (hipStream_t)stream)
             : attn::launch_bwd16(p, dtype == ATTN_BF16, (int)d, causal != 0, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the row statistic D (B*H*N floats), which
+// attn_bwd keeps in the caller's `delta`, lives in this file-scope device
+// array instead. Each device holds its own copy from the library's load to
+// the end of the process. In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the address hipGetSymbolAddress returns for
+// the current device, fetched once per device on its first call.
+static __device__ __align__(256) float scratch[ATTN_BWD_NOALLOC_MAX_ROWS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, or nullptr on a HIP
+// error (the error code goes to *err).
+float* device_scratch(hipError_t* err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess || !ptr) {
+            if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = (float*)ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                                int causal, float scale, int dtype, void* stream) {
+    // attn_bwd's checks and the size limit of the static array, before any
+    // HIP call.
+    const int rc = validate_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, causal,
+                                scale, dtype);
+    if (rc != ATTN_OK) return rc;
+    if (B * H > ATTN_BWD_NOALLOC_MAX_ROWS / N) return ATTN_ETOOBIG;
+    hipError_t e;
+    float* delta = device_scratch(&e);
+    if (!delta) return ATTN_EHIP;
+    return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, H_kv, N, d, causal, scale,
+                    dtype, stream);
 }
 
 extern "C" int64_t attn_unfused_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype) {
@@ -161,6 +233,9 @@ extern "C" const char* attn_strerror(int code) {
         case ATTN_EUNSUPPORTED: return "unsupported head dimension (need 64 or 128)";
         case ATTN_EALIGN: return "a tensor pointer is misaligned (16 bytes; lse, delta 4; workspace 256)";
         case ATTN_EHIP: return "HIP kernel launch failed";
+        case ATTN_ETOOBIG:
+            return "B*H*N exceeds the static row-statistic array of attn_bwd_noalloc "
+                   "(ATTN_BWD_NOALLOC_MAX_ROWS)";
         default: return "unknown error code";
     }
 }

@@ -42,8 +42,13 @@ enum {
     ATTN_EINVAL = -1,       /* bad argument (null pointer, size, H_kv, dtype, scale, causal) */
     ATTN_EUNSUPPORTED = -2, /* head dimension other than 64 or 128 */
     ATTN_EALIGN = -3,       /* a base pointer misaligned (see each function) */
-    ATTN_EHIP = -4          /* the HIP launch failed */
+    ATTN_EHIP = -4,         /* the HIP launch failed */
+    ATTN_ETOOBIG = -5       /* attn_bwd_noalloc: B*H*N > ATTN_BWD_NOALLOC_MAX_ROWS */
 };
+
+/* Rows (B*H*N) the static row-statistic array of attn_bwd_noalloc holds:
+ * 4 Mi floats, 16 MiB of device memory per GPU the library runs on. */
+#define ATTN_BWD_NOALLOC_MAX_ROWS (4 * 1024 * 1024)
 
 /*
  * attn_fwd — exact attention forward on the GPU.
@@ -143,6 +148,29 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, void* dq, void* dk, void* dv, float* delta,
              int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int causal,
              float scale, int dtype, void* stream);
+
+/*
+ * attn_bwd_noalloc — attn_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, kernels and results, without the
+ * `delta` argument. The row statistic D_i (B*H*N floats) is kept in a
+ * static device array of ATTN_BWD_NOALLOC_MAX_ROWS floats that each GPU
+ * holds from the library's load until the process ends; the call performs
+ * no hipMalloc, hipFree or other allocation.
+ *
+ * Arguments as for attn_bwd, without delta.
+ * Errors: as attn_bwd (validation before any HIP call), plus ATTN_ETOOBIG
+ * when B*H*N > ATTN_BWD_NOALLOC_MAX_ROWS; ATTN_EHIP also if the static
+ * array's device address cannot be obtained.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (D is written in full before it is read, so nothing needs
+ * clearing). Calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race on the array: serialise them.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int causal,
+                     float scale, int dtype, void* stream);
 
 /*
  * attn_fwd_unfused — the same forward pass (multi-head, H_kv = H) computed

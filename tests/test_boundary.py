@@ -45,8 +45,8 @@ def test_every_header_is_covered():
 
 def test_attn_library_exports_header(attn_lib_path):
     decl = _declared_functions("attn.h")
-    assert decl == ["attn_bwd", "attn_fwd", "attn_fwd_gqa", "attn_fwd_unfused", "attn_strerror",
-                    "attn_unfused_workspace_bytes"]
+    assert decl == ["attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_gqa", "attn_fwd_unfused",
+                    "attn_strerror", "attn_unfused_workspace_bytes"]
     missing = set(decl) - _exported(attn_lib_path)
     assert not missing, missing
     ctypes.CDLL(attn_lib_path)   # loads without a GPU
@@ -173,6 +173,42 @@ def test_bwd_argument_validation(attn_lib_path):
         a = dict(good, **change)
         rc = ea.attn_bwd(*(a[n] for n in names))
         assert rc == want, (change, rc)
+
+
+def test_bwd_noalloc_argument_validation(attn_lib_path):
+    """attn_bwd_noalloc: attn_bwd's checks (no delta argument) and the size
+    limit of its static row-statistic array, all before any HIP call (the
+    pointers here are never dereferenced)."""
+    import exact_attention_15_amd as ea
+    P = 0x7f0000000000
+    good = dict(q=P, k=P + 0x1000, v=P + 0x2000, o=P + 0x3000, lse=P + 0x4000, dout=P + 0x5000,
+                dq=P + 0x6000, dk=P + 0x7000, dv=P + 0x8000,
+                B=1, H=4, H_kv=2, N=128, d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16,
+                stream=None)
+    limit = ea.BWD_NOALLOC_MAX_ROWS
+    cases = [
+        (dict(q=None), ea.ATTN_EINVAL),
+        (dict(lse=None), ea.ATTN_EINVAL),
+        (dict(dout=None), ea.ATTN_EINVAL),
+        (dict(dv=None), ea.ATTN_EINVAL),
+        (dict(H_kv=3), ea.ATTN_EINVAL),
+        (dict(N=0), ea.ATTN_EINVAL),
+        (dict(dtype=5), ea.ATTN_EINVAL),
+        (dict(d=96), ea.ATTN_EUNSUPPORTED),
+        (dict(dq=P + 0x6004), ea.ATTN_EALIGN),
+        (dict(B=1, H=1, H_kv=1, N=limit + 1), ea.ATTN_ETOOBIG),
+        (dict(B=2, H=2, H_kv=2, N=limit // 4 + 1), ea.ATTN_ETOOBIG),
+        (dict(B=65, H=65536, H_kv=65536, N=1), ea.ATTN_ETOOBIG),
+        # an invalid argument is reported before the size limit
+        (dict(B=1, H=1, H_kv=1, N=limit + 1, dtype=7), ea.ATTN_EINVAL),
+    ]
+    names = ["q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "B", "H", "H_kv",
+             "N", "d", "causal", "scale", "dtype", "stream"]
+    for change, want in cases:
+        a = dict(good, **change)
+        rc = ea.attn_bwd_noalloc(*(a[n] for n in names))
+        assert rc == want, (change, rc)
+    assert "ATTN_BWD_NOALLOC_MAX_ROWS" in ea.strerror(ea.ATTN_ETOOBIG)
 
 
 def test_unfused_workspace_and_validation(attn_lib_path):
