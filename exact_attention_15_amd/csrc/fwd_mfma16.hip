@@ -53,7 +53,10 @@
 //         VALU step j : softmax of S(j) -> P(j), rescale of O when needed
 //     with a workgroup barrier after every step, group B one step behind,
 //     so in every barrier interval one wave of each SIMD feeds the matrix
-//     core while the other runs the softmax on the vector ALU.
+//     core while the other runs the softmax on the vector ALU. At d = 64
+//     with one query block the MFMA step does the P.V products first: the
+//     registers the S products are about to fill stage the V^T operands
+//     read ahead, and the P registers then stage the K operands.
 //   * Lazy rescale: the exponent base m only moves when a tile's row max
 //     exceeds it by more than 2^8 in probability; otherwise P <= 256 is used
 //     as is. The final O / l does not depend on the base, and a bf16/fp16 P
@@ -177,8 +180,10 @@ __device__ __forceinline__ float permlane16_swap_y(float x, float y) {
     return __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// d = 64 with one query block: four waves per SIMD (two workgroups per
+// compute unit), i.e. at most 128 VGPRs; the others take two waves per SIMD.
 template <bool IS_BF16, int D, bool CAUSAL, int QB>
-__global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_kernel(FwdParams p) {
     static_assert(QB == 1 || (QB == 2 && D == 64), "two query blocks per wave only at d = 64");
     using Op = Op16<IS_BF16>;
     using T = Tile<D>;
@@ -344,64 +349,120 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
         constexpr bool HAS_PV = decltype(has_pv_tag)::value;
         const LDS_AS char* kb_base = (const LDS_AS char*)(KPAR ? k_lds1 : k_lds0);
         const LDS_AS char* vb_base = (const LDS_AS char*)(KPAR ? v_lds0 : v_lds1);
-        // S is computed for every tile, also ones this wave does not need
-        // (their S is never read): a conditional S would cost register copies.
-        // The two key blocks' products alternate, so that consecutive MFMAs
-        // share their Q operand (each accumulator still sums over d in
-        // order): fewer operand bits toggle, and under the power limit that
-        // is clock (+0.5 % at d = 128 and at fp16 N = 16k).
+        if constexpr (D == 64 && QB == 1) {
+            // P.V of the previous tile first, then S. At 126 registers the
+            // wave has no spare ones to read operands ahead, but the S
+            // accumulators are dead until the S products (their last values
+            // became P in the softmax step) and P is dead after the P.V
+            // products: the V^T fragments are read ahead into the former,
+            // the K fragments into the latter, four fragments ahead each,
+            // so the MFMAs do not wait for LDS one by one (measured: +3 % at
+            // the causal headline; at d = 128 the S-first order below is
+            // kept, it measured 0.5 % faster there).
+            if (HAS_PV && jj - 1 < n_live) {
+                constexpr int NF = 4 * NDB;   // V^T fragments
+                constexpr int PF = 4;         // read ahead
+                u32x4 vf[NF];
 #pragma unroll
-        for (int kd = 0; kd < NKD; ++kd)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 a = *(const LDS_AS u32x4*)(kb_base + koff[kd] + kb * 32 * T::kRowBytes);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    s[qb][kb] = Op::mfma(a, qf[qb][kd], kd == 0 ? f32x16{} : s[qb][kb]);
-            }
-        // Order: three K fragment reads ahead, then one more read per QB
-        // MFMAs, so that LDS latency hides behind the matrix core.
-        constexpr int kSReads = 2 * NKD;
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
-#pragma unroll
-        for (int r = 3; r < kSReads; ++r) {
-            __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 3 * QB, 1);
-        // Keeps the P.V operand reads from being hoisted over the S products
-        // (more live registers than the wave has).
-        __builtin_amdgcn_sched_barrier(0);
-        // P of a tile past this wave's rows is all zero, so its P.V is skipped.
-        if (HAS_PV && jj - 1 < n_live) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < 4; ++kb2)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) lacc[qb] = Op::mfma16(ones, pk[qb][kb2], lacc[qb]);
-            // d blocks innermost: consecutive MFMAs share their P operand.
-#pragma unroll
-            for (int kb2 = 0; kb2 < 4; ++kb2)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const LDS_AS char* a0 = vb_base + voff[db] + (16 * kb2) * T::kRowBytes;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * T::kRowBytes));
-                    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) o[qb][db] = Op::mfma(a, pk[qb][kb2], o[qb][db]);
+                for (int f = 0; f < NF; ++f) {
+                    const LDS_AS char* a0 = vb_base + voff[f % NDB] + (16 * (f / NDB)) * T::kRowBytes;
+                    vf[f] = tr_read(a0, a0 + 8 * T::kRowBytes);
                 }
-            // Order: two V^T fragments (four reads) ahead, the row-sum MFMAs
-            // (no LDS operand) while they arrive, then one fragment per QB
-            // MFMAs.
-            constexpr int kVFrags = 4 * NDB;
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
-            __builtin_amdgcn_sched_group_barrier(0x008, 4 * QB, 2);
+                // The row-sum MFMAs (no LDS operand) cover the first reads.
 #pragma unroll
-            for (int f = 2; f < kVFrags; ++f) {
-                __builtin_amdgcn_sched_group_barrier(0x008, QB, 2);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+                for (int kb2 = 0; kb2 < 4; ++kb2) lacc[0] = Op::mfma16(ones, pk[0][kb2], lacc[0]);
+                // d blocks innermost: consecutive MFMAs share their P operand.
+#pragma unroll
+                for (int f = 0; f < NF; ++f) o[0][f % NDB] = Op::mfma(vf[f], pk[0][f / NDB], o[0][f % NDB]);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 2);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
+#pragma unroll
+                for (int f = PF; f < NF; ++f) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, PF, 2);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 2);
+            // S for every tile, also ones past this wave's rows (never read).
+            // The two key blocks' products alternate: consecutive MFMAs
+            // share their Q operand.
+#pragma unroll
+            for (int kd = 0; kd < NKD; ++kd)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const u32x4 a = *(const LDS_AS u32x4*)(kb_base + koff[kd] + kb * 32 * T::kRowBytes);
+                    s[0][kb] = Op::mfma(a, qf[0][kd], kd == 0 ? f32x16{} : s[0][kb]);
+                }
+            constexpr int kSReads = 2 * NKD, KF = 4;
+            __builtin_amdgcn_sched_group_barrier(0x100, KF, 3);
+#pragma unroll
+            for (int r = KF; r < kSReads; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, KF, 3);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            // S is computed for every tile, also ones this wave does not need
+            // (their S is never read): a conditional S would cost register copies.
+            // The two key blocks' products alternate, so that consecutive MFMAs
+            // share their Q operand (each accumulator still sums over d in
+            // order): fewer operand bits toggle, and under the power limit that
+            // is clock (+0.5 % at d = 128 and at fp16 N = 16k).
+    #pragma unroll
+            for (int kd = 0; kd < NKD; ++kd)
+    #pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const u32x4 a = *(const LDS_AS u32x4*)(kb_base + koff[kd] + kb * 32 * T::kRowBytes);
+    #pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        s[qb][kb] = Op::mfma(a, qf[qb][kd], kd == 0 ? f32x16{} : s[qb][kb]);
+                }
+            // Order: three K fragment reads ahead, then one more read per QB
+            // MFMAs, so that LDS latency hides behind the matrix core.
+            constexpr int kSReads = 2 * NKD;
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
+    #pragma unroll
+            for (int r = 3; r < kSReads; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, QB, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 3 * QB, 1);
+            // Keeps the P.V operand reads from being hoisted over the S products
+            // (more live registers than the wave has).
+            __builtin_amdgcn_sched_barrier(0);
+            // P of a tile past this wave's rows is all zero, so its P.V is skipped.
+            if (HAS_PV && jj - 1 < n_live) {
+    #pragma unroll
+                for (int kb2 = 0; kb2 < 4; ++kb2)
+    #pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) lacc[qb] = Op::mfma16(ones, pk[qb][kb2], lacc[qb]);
+                // d blocks innermost: consecutive MFMAs share their P operand.
+    #pragma unroll
+                for (int kb2 = 0; kb2 < 4; ++kb2)
+    #pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const LDS_AS char* a0 = vb_base + voff[db] + (16 * kb2) * T::kRowBytes;
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)a0);
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(a0 + 8 * T::kRowBytes));
+                        const u32x4 a = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    #pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) o[qb][db] = Op::mfma(a, pk[qb][kb2], o[qb][db]);
+                    }
+                // Order: two V^T fragments (four reads) ahead, the row-sum MFMAs
+                // (no LDS operand) while they arrive, then one fragment per QB
+                // MFMAs.
+                constexpr int kVFrags = 4 * NDB;
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * QB, 2);
+    #pragma unroll
+                for (int f = 2; f < kVFrags; ++f) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, QB, 2);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 2);
+            }
         }
         // (jj < n_tiles is implied by jj < n_live; stated, it lets the
         // compiler drop this from the last step, whose S is never used.)
@@ -415,7 +476,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd16_kernel(FwdParams p) {
     // maximum with the other block's exponentials: v_exp_f32, one per ~23
     // cycles of a wave, is what bounds this step.
     auto valu_step = [&](int jj) __attribute__((always_inline)) {
-        if (jj >= n_live) return;
+        if (jj >= n_live) {
+            // Past this wave's rows: no P. At d = 64 with one query block,
+            // defining the P registers anyway ends the previous P's life at
+            // the P.V products that read it (otherwise the compiler keeps it
+            // across the next S products), which frees them for the K
+            // fragments read ahead there.
+            if constexpr (D == 64 && QB == 1) {
+#pragma unroll
+                for (int kb2 = 0; kb2 < 4; ++kb2) pk[0][kb2] = u32x4{0u, 0u, 0u, 0u};
+            }
+            return;
+        }
         if (!kMaxInMfmaStep) mask_and_max(jj);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
