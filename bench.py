@@ -256,165 +256,177 @@ def median_launch_ms(fn, n: int = 200) -> float:
     return ts[n // 2]
 
 
-def device_state_under_load(fn, seconds: float = 2.0, ms_per_call: float = 0.1):
-    """GFX clock (MHz) and socket power (W), medians of amdsmi readings taken
-    while launches of fn keep the GPU busy (outside the timed region), the
-    board's power cap (W), and the share of that time the firmware held the
-    clock down for package power (its PPT violation counter over its tick
-    counter). amdsmi's readings trail the load by up to about a second, so
-    launches run without a break for `seconds` and only the second half
-    counts; each reading is taken with ~25 ms of launches queued and kept
-    only while the stream still has work pending. Read-only queries; each
-    field None where amdsmi is missing or refuses it."""
-    import torch
-    state = {"gfx_clock_mhz": None, "socket_power_w": None, "power_cap_w": None,
-             "power_limited_frac": None}
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-        h = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
-    except Exception:
-        return state
+class _Smi:
+    """Read-only amdsmi queries for the current device; every method returns
+    None where amdsmi is missing or refuses the query."""
 
-    def _try(f, *a):
+    # Accumulated throttle counters of amdsmi_get_violation_status, each a
+    # count of firmware ticks (acc_counter) spent under that limit.
+    LIMITS = {"ppt_pwr": "acc_ppt_pwr", "socket_thrm": "acc_socket_thrm",
+              "prochot_thrm": "acc_prochot_thrm", "vr_thrm": "acc_vr_thrm",
+              "hbm_thrm": "acc_hbm_thrm", "gfx_clk_below_host_limit": "acc_gfx_clk_below_host_limit"}
+
+    def __init__(self):
+        import torch
+        self.ok = False
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.h = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
+            self.ok = True
+        except Exception:
+            pass
+
+    def _try(self, f, *a):
+        if not self.ok:
+            return None
         try:
             return f(*a)
         except Exception:
             return None
 
-    def _violation():
-        v = _try(amdsmi.amdsmi_get_violation_status, h)
-        if not isinstance(v, dict):
-            return None
-        ppt, ticks = v.get("acc_ppt_pwr"), v.get("acc_counter")
-        ok = isinstance(ppt, int) and isinstance(ticks, int)
-        return (ppt, ticks) if ok else None
+    def clock_mhz(self):
+        info = self._try(self.amdsmi.amdsmi_get_clock_info, self.h, self.amdsmi.AmdSmiClkType.GFX) \
+            if self.ok else None
+        clk = info.get("clk") if isinstance(info, dict) else None
+        return float(clk) if isinstance(clk, (int, float)) and clk > 0 else None
 
-    cap = _try(amdsmi.amdsmi_get_power_cap_info, h)
-    if isinstance(cap, dict) and isinstance(cap.get("power_cap"), (int, float)) and cap["power_cap"] > 0:
-        state["power_cap_w"] = round(cap["power_cap"] / 1e6, 1)   # reported in microwatts
-    clocks, powers, v0 = [], [], None
-    try:
-        stream = torch.cuda.current_stream()
-        per_sample = max(10, int(25.0 / max(ms_per_call, 1e-3)))
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            for _ in range(per_sample):
-                fn()
-            if time.perf_counter() - t0 < seconds / 2:
-                continue
-            if v0 is None:
-                v0 = _violation() or (None,)
-            info = _try(amdsmi.amdsmi_get_clock_info, h, amdsmi.AmdSmiClkType.GFX)
-            pw = _try(amdsmi.amdsmi_get_power_info, h)
-            busy = not stream.query()
-            clk = info.get("clk") if isinstance(info, dict) else None
-            sp = pw.get("socket_power") if isinstance(pw, dict) else None
-            if busy and isinstance(clk, (int, float)) and clk > 0:
-                clocks.append(float(clk))
-            if busy and isinstance(sp, (int, float)) and sp > 0:
-                powers.append(float(sp))
-        v1 = _violation()
-        torch.cuda.synchronize()
-    except Exception:
+    def socket_power_w(self):
+        pw = self._try(self.amdsmi.amdsmi_get_power_info, self.h) if self.ok else None
+        sp = pw.get("socket_power") if isinstance(pw, dict) else None
+        return float(sp) if isinstance(sp, (int, float)) and sp > 0 else None
+
+    def power_cap_w(self):
+        cap = self._try(self.amdsmi.amdsmi_get_power_cap_info, self.h) if self.ok else None
+        c = cap.get("power_cap") if isinstance(cap, dict) else None
+        return round(c / 1e6, 1) if isinstance(c, (int, float)) and c > 0 else None   # microwatts
+
+    def hotspot_c(self):
+        if not self.ok:
+            return None
+        a = self.amdsmi
+        t = self._try(a.amdsmi_get_temp_metric, self.h, a.AmdSmiTemperatureType.HOTSPOT,
+                      a.AmdSmiTemperatureMetric.CURRENT)
+        return float(t) if isinstance(t, (int, float)) else None
+
+    def violations(self):
+        v = self._try(self.amdsmi.amdsmi_get_violation_status, self.h) if self.ok else None
+        if not isinstance(v, dict) or not isinstance(v.get("acc_counter"), int):
+            return None
+        out = {"ticks": v["acc_counter"]}
+        for name, key in self.LIMITS.items():
+            if isinstance(v.get(key), int):
+                out[name] = v[key]
+        return out
+
+    @staticmethod
+    def limit_fracs(v0, v1):
+        """Share of the ticks between two violation readings spent under each limit."""
+        if not v0 or not v1 or v1["ticks"] <= v0["ticks"]:
+            return None
+        dt = v1["ticks"] - v0["ticks"]
+        return {k: round((v1[k] - v0[k]) / dt, 3) for k in v1 if k != "ticks" and k in v0}
+
+    def close(self):
+        self._try(self.amdsmi.amdsmi_shut_down) if self.ok else None
+
+
+def device_state_under_load(smi, fn, seconds: float = 2.0, ms_per_call: float = 0.1):
+    """GFX clock (MHz), socket power (W) and hotspot temperature, medians of
+    amdsmi readings taken while launches of fn keep the GPU busy, and the
+    share of that time the firmware held the clock down under each of its
+    limits (package power, socket / VR / HBM temperature, PROCHOT, below the
+    host's clock limit). amdsmi's readings trail the load by up to about a
+    second, so launches run without a break for `seconds` and only the
+    second half counts; each reading is taken with ~25 ms of launches queued
+    and kept only while the stream still has work pending."""
+    import torch
+    state = {"gfx_clock_mhz": None, "socket_power_w": None, "hotspot_c": None,
+             "limit_fracs": None}
+    if not smi.ok:
         return state
-    finally:
-        _try(amdsmi.amdsmi_shut_down)
-    if clocks:
-        state["gfx_clock_mhz"] = sorted(clocks)[len(clocks) // 2]
-    if powers:
-        state["socket_power_w"] = sorted(powers)[len(powers) // 2]
-    if v0 and v0[0] is not None and v1 and v1[1] > v0[1]:
-        state["power_limited_frac"] = round((v1[0] - v0[0]) / (v1[1] - v0[1]), 3)
+    clocks, powers, temps, v0 = [], [], [], None
+    stream = torch.cuda.current_stream()
+    per_sample = max(10, int(25.0 / max(ms_per_call, 1e-3)))
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(per_sample):
+            fn()
+        if time.perf_counter() - t0 < seconds / 2:
+            continue
+        if v0 is None:
+            v0 = smi.violations()
+        clk, sp, tc = smi.clock_mhz(), smi.socket_power_w(), smi.hotspot_c()
+        if not stream.query():
+            clocks += [clk] if clk else []
+            powers += [sp] if sp else []
+            temps += [tc] if tc is not None else []
+    v1 = smi.violations()
+    torch.cuda.synchronize()
+    med = lambda xs: sorted(xs)[len(xs) // 2] if xs else None   # noqa: E731
+    state.update(gfx_clock_mhz=med(clocks), socket_power_w=med(powers), hotspot_c=med(temps),
+                 limit_fracs=smi.limit_fracs(v0, v1))
     return state
 
 
-def _time_calls(fn, steps, warmup):
-    import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
-        fn()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps, time.perf_counter() - t_wall
+class ClockSampler:
+    """Polls the GFX clock from a second thread (amdsmi calls release the
+    interpreter lock), one reading every ~0.5 ms with its host time, so
+    that the readings inside any host-time window (the timed region) can be
+    picked afterwards. It is started before the warm-up: no amdsmi call then
+    separates the warm-up from the timed region (an idle gap of a few ms
+    there measurably slows the first launches after it)."""
+
+    def __init__(self, smi):
+        import threading
+        self.smi, self.samples, self._stop = smi, [], threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True) if smi.ok else None
+
+    def _run(self):
+        while not self._stop.wait(0.0005):
+            c = self.smi.clock_mhz()
+            if c:
+                self.samples.append((time.perf_counter(), c))
+
+    def __enter__(self):
+        if self._t:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._t:
+            self._t.join()
+        return False
+
+    def window(self, t0, t1):
+        """(median, count) of the readings taken between host times t0, t1."""
+        xs = sorted(c for t, c in self.samples if t0 <= t <= t1)
+        return (xs[len(xs) // 2] if xs else None), len(xs)
 
 
-def run_unfused(args, name, w):
-    """Unfused-versus-fused comparison line (``--pass unfused``)."""
+class _NoSmi(_Smi):
+    def __init__(self):
+        self.ok = False
+
+
+def parity_stats(w, q, k, v, o, lse, n_rows: int = 2048):
+    """O and lse against the oracle on sampled rows (the first 8 and n_rows
+    drawn at random): O max-abs and mean-abs error, the noise-to-signal
+    ratio ||O - O_ref|| / ||O_ref|| and the lse max-abs error."""
     import numpy as np
-    import torch
-
-    import exact_attention_15_amd as ea
-    from exact_attention_15_amd.inputs import workload_inputs
-
-    dt_name = DTYPE_NAME[str(w.dtype)]
-    elem = 4 if dt_name == "fp32" else 2
-    ea.load_library()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    q, k, v = workload_inputs(w)
-    qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    ws = torch.empty(ea.unfused_workspace_bytes(w.B, w.H, w.N, ea.dtype_code(w.dtype)),
-                     dtype=torch.uint8, device=dev)
-    o, lse = ea.fwd_unfused(qd, kd, vd, causal=w.causal, scale=w.scale, workspace=ws)
-    torch.cuda.synchronize()
-    parity = None
-    if not args.no_check:
-        import oracle
-        rng = np.random.default_rng(1)
-        rows = np.unique(np.concatenate([np.arange(8), rng.integers(0, w.B * w.H * w.N, 56)]))
-        o_ref, _ = oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows)
-        parity = float(np.abs(o.cpu().double().numpy().reshape(-1, w.d)[rows] - o_ref).max())
-        if not parity <= (1e-4 if elem == 4 else 2e-2):
-            print(f"bench.py: unfused parity gate failed: {parity:.3e}", file=sys.stderr)
-            sys.exit(1)
-    steps = max(1, args.steps // 10)
-    ms_u, t_wall = _time_calls(lambda: ea.fwd_unfused(qd, kd, vd, causal=w.causal,
-                                                      scale=w.scale, workspace=ws),
-                               steps, max(1, args.warmup // 10))
-    out = (torch.empty_like(qd), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev))
-    ms_f, _ = _time_calls(lambda: ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out),
-                          args.steps, args.warmup)
-    flops = attention_flops(w.B, w.H, w.N, w.d, w.causal)
-    tflops = flops / (ms_u * 1e-3) / 1e12
-    ld = (w.N + 63) // 64 * 64
-    # The method's own traffic: S written and read (fp32), P written and read
-    # (in the input type), plus Q, K, V read and O, lse written.
-    mbytes = (w.B * w.H * w.N * ld * (4 + 4 + 2 * elem)
-              + algorithmic_bytes(w.B, w.H, w.N, w.d, elem))
-    gbs = mbytes / (ms_u * 1e-3) / 1e9
-    line = {
-        "metric": "unfused attention fwd TFLOPS (S, softmax, P V as three kernels)",
-        "value": round(tflops, 2),
-        "unit": "TFLOPS",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": max(1, args.warmup // 10),
-        "ms_per_step": round(ms_u, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dt_name,
-        "data": "synthetic (seeded i.i.d. N(0,1) inputs rounded to the dtype)",
-        "config": {"workload": w.describe() + " (unfused)", "name": name, "B": w.B, "H": w.H,
-                   "N": w.N, "d": w.d, "causal": w.causal, "scale": w.scale},
-        # The unfused path is bound by its N x N traffic.
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
-        "fused_ms_per_step": round(ms_f, 5),
-        "fused_tflops": round(flops / (ms_f * 1e-3) / 1e12, 2),
-        "fusion_speedup": round(ms_u / ms_f, 2),
-        "parity_o_max_abs_sampled": parity,
-        "wall_s_timed_region": round(t_wall, 4),
-    }
-    print(json.dumps(line), flush=True)
+    import oracle
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([np.arange(8), rng.integers(0, w.B * w.H * w.N, n_rows)]))
+    o_ref, l_ref = oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows)
+    o_got = o.cpu().double().numpy().reshape(-1, w.d)[rows]
+    l_got = lse.cpu().double().numpy().reshape(-1)[rows]
+    diff = np.abs(o_got - o_ref)
+    return {"rows": int(len(rows)), "o_max_abs": float(diff.max()),
+            "o_mean_abs": float(diff.mean()),
+            "o_nsr": float(np.linalg.norm(o_got - o_ref) / np.linalg.norm(o_ref)),
+            "lse_max_abs": float(np.abs(l_got - l_ref).max())}
 
 
 def main():
@@ -481,43 +493,66 @@ def main():
     o = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     out = (o, lse)
-
-    for _ in range(args.warmup):
-        ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out)
+    # One step is one attn_fwd_gqa call. The wrapper's checks run once
+    # (through ea.fwd, whose result the parity gate reads); the timed calls
+    # pass the same validated pointers straight to the C entry point, so the
+    # host enqueues each launch in a few microseconds and the GPU does not
+    # wait on Python between launches.
+    ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out)
     torch.cuda.synchronize()
+    lib = ea.load_library()
+    c_args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
+              w.kv_heads, w.N, w.d, int(w.causal), w.scale, ea.dtype_code(w.dtype),
+              torch.cuda.current_stream(dev).cuda_stream)
 
-    parity = None
+    def step_fn():
+        rc = lib.attn_fwd_gqa(*c_args)
+        if rc != 0:
+            raise ea.AttnError(rc, ea.strerror(rc), "attn_fwd_gqa")
+
+    # Parity gate on the first launch, before anything is timed: sampled rows
+    # against the oracle, with the error statistics reported in the line.
+    errs = None
     if not args.no_check:
-        import oracle
-        rng = np.random.default_rng(1)
-        rows = np.unique(np.concatenate([np.arange(8), rng.integers(0, w.B * w.H * w.N, 56)]))
-        o_ref, l_ref = oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows)
-        o_got = o.cpu().double().numpy().reshape(-1, w.d)[rows]
-        parity = float(np.abs(o_got - o_ref).max())
+        errs = parity_stats(w, q, k, v, o, lse)
         tol = 1e-4 if dt_name == "fp32" else 2e-2
-        if not parity <= tol:
-            print(f"bench.py: parity gate failed: O max-abs {parity:.3e} > {tol}", file=sys.stderr)
+        if not errs["o_max_abs"] <= tol:
+            print(f"bench.py: parity gate failed: O max-abs {errs['o_max_abs']:.3e} > {tol}",
+                  file=sys.stderr)
             sys.exit(1)
 
-    # Timed region: barrier-equivalent sync, K launches bracketed by HIP events
-    # recorded on the stream the kernels run on, sync.
+    # Per-launch median and the device's sustained state under this load
+    # (clock, power, temperature, throttle shares), measured before the
+    # warm-up: the GPU then enters the warm-up and the timed region already
+    # at its sustained clock.
+    smi = _Smi()
+    ms_median = median_launch_ms(step_fn)
+    dev_state = (device_state_under_load(smi, step_fn, ms_per_call=ms_median)
+                 if not args.no_device_state else
+                 dict.fromkeys(("gfx_clock_mhz", "socket_power_w", "hotspot_c", "limit_fracs")))
+
+    # Warm-up, then the timed region: barrier-equivalent sync, K launches
+    # bracketed by HIP events recorded on the stream the kernels run on, sync.
+    # A second thread reads the GFX clock meanwhile.
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
+    with ClockSampler(smi if not args.no_device_state else _NoSmi()) as clk:
+        for _ in range(args.warmup):
+            step_fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(args.steps):
+            step_fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    t_wall = t1 - t0
     ms = start.elapsed_time(stop) / args.steps
-    step_fn = lambda: ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out)   # noqa: E731
-    ms_median = median_launch_ms(step_fn)
-    dev_state = (device_state_under_load(step_fn, ms_per_call=ms_median) if not args.no_device_state
-                 else dict.fromkeys(("gfx_clock_mhz", "socket_power_w", "power_cap_w",
-                                     "power_limited_frac")))
+    clk_timed, clk_n = clk.window(t0, t1)
+    power_cap = smi.power_cap_w()
+    smi.close()
 
     flops = attention_flops(w.B, w.H, w.N, w.d, w.causal)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -525,6 +560,7 @@ def main():
     abytes = algorithmic_bytes(w.B, w.H, w.N, w.d, elem, w.kv_heads)
     peak = PEAK_TFLOPS[dt_name]
     traffic = measured_traffic(name)
+    lf = dev_state["limit_fracs"] or {}
 
     line = {
         "metric": "attention fwd TFLOPS (bf16, causal, N=4096 d=64); % of MFMA peak",
@@ -547,13 +583,17 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": traffic},
         "ms_median_launch": round(ms_median, 5),
+        "gfx_clock_mhz_timed_region": clk_timed,
+        "gfx_clock_samples_timed_region": clk_n,
         "gfx_clock_mhz_under_load": dev_state["gfx_clock_mhz"],
         "socket_power_w_under_load": dev_state["socket_power_w"],
-        "power_cap_w": dev_state["power_cap_w"],
-        "power_limited_frac_under_load": dev_state["power_limited_frac"],
+        "hotspot_c_under_load": dev_state["hotspot_c"],
+        "power_cap_w": power_cap,
+        "power_limited_frac_under_load": lf.get("ppt_pwr"),
+        "limit_fracs_under_load": dev_state["limit_fracs"],
         "algorithmic_gb_s": round(abytes / (ms * 1e-3) / 1e9, 1),
         "exp_per_s": (w.B * w.H * w.N * w.N / (2 if w.causal else 1)) / (ms * 1e-3),
-        "parity_o_max_abs_sampled": parity,
+        "parity_sampled": errs,
         "wall_s_timed_region": round(t_wall, 4),
     }
     if not args.no_cpu_baseline:

@@ -45,12 +45,29 @@ def test_traffic_is_tied_to_the_kernel_sources():
 
 
 def test_device_state_degrades_to_nulls_without_a_device():
-    """The clock / power sampler is outside the timed region and must never
+    """The clock / power sampler runs outside the timed region and must never
     fail a bench run: without a GPU (or without amdsmi) every field is None,
-    and the function returns without calling the step."""
+    and the function returns without calling the step; the timed-region
+    clock sampler then collects nothing."""
     calls = []
-    state = bench.device_state_under_load(lambda: calls.append(1), seconds=0.05)
-    assert set(state) == {"gfx_clock_mhz", "socket_power_w", "power_cap_w", "power_limited_frac"}
-    import torch
-    if not torch.cuda.is_available():
-        assert all(v is None for v in state.values()) and not calls
+    smi = bench._NoSmi()
+    state = bench.device_state_under_load(smi, lambda: calls.append(1), seconds=0.05)
+    assert set(state) == {"gfx_clock_mhz", "socket_power_w", "hotspot_c", "limit_fracs"}
+    assert all(v is None for v in state.values()) and not calls
+    with bench.ClockSampler(smi) as clk:
+        pass
+    assert clk.window(0.0, 1e30) == (None, 0) and clk.samples == []
+
+
+def test_clock_window_picks_readings_by_host_time():
+    clk = bench.ClockSampler(bench._NoSmi())
+    clk.samples = [(1.0, 2100.0), (2.0, 1900.0), (3.0, 1800.0), (4.0, 1850.0), (9.0, 2400.0)]
+    assert clk.window(2.0, 4.0) == (1850.0, 3)
+    assert clk.window(5.0, 8.0) == (None, 0)
+
+
+def test_limit_fractions():
+    v0 = {"ticks": 100, "ppt_pwr": 10, "socket_thrm": 0}
+    v1 = {"ticks": 300, "ppt_pwr": 110, "socket_thrm": 50}
+    assert bench._Smi.limit_fracs(v0, v1) == {"ppt_pwr": 0.5, "socket_thrm": 0.25}
+    assert bench._Smi.limit_fracs(v0, v0) is None
