@@ -68,7 +68,8 @@ extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o
     p.BH_kv = (int)(B * H_kv);
     p.H_kv = (int)H_kv;
     p.G = (int)(H / H_kv);
-    p.n_qtiles = 0;   // set by the launcher for its own query tile
+    p.n_qtiles = 0;    // set by the launcher for its own query tile
+    p.xcd_order = 0;   // chosen by the launcher
     // scale * log2(e), rounded once to fp32: scores go straight into exp2.
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 

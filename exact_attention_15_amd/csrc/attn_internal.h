@@ -19,6 +19,7 @@ struct FwdParams {
     int H_kv;           // key/value heads; H_kv divides H
     int G;              // H / H_kv query heads per key/value head
     int n_qtiles;       // ceil(N / query-tile rows)
+    int xcd_order;      // 1: XCD-major work order (fwd_order.h), 0: tile-major
     float scale_log2;   // scale * log2(e): scores enter exp2 directly
 };
 
