@@ -46,6 +46,7 @@ COUNTER_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_counters.txt")
 # Sources of the kernel the committed counters were taken on (the bf16 /
 # fp16 forward, its launcher and the entry point).
 KERNEL_SOURCES = ["exact_attention_15_amd/csrc/fwd_mfma16.hip",
+                  "exact_attention_15_amd/csrc/fwd_order.h",
                   "exact_attention_15_amd/csrc/mfma_common.h",
                   "exact_attention_15_amd/csrc/attn_api.hip",
                   "exact_attention_15_amd/csrc/attn_internal.h"]
