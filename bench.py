@@ -407,6 +407,94 @@ class ClockSampler:
         return (xs[len(xs) // 2] if xs else None), len(xs)
 
 
+def _time_calls(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps, time.perf_counter() - t_wall
+
+
+def run_unfused(args, name, w):
+    """Unfused-versus-fused comparison line (``--pass unfused``)."""
+    import numpy as np
+    import torch
+
+    import exact_attention_15_amd as ea
+    from exact_attention_15_amd.inputs import workload_inputs
+
+    dt_name = DTYPE_NAME[str(w.dtype)]
+    elem = 4 if dt_name == "fp32" else 2
+    ea.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = workload_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    ws = torch.empty(ea.unfused_workspace_bytes(w.B, w.H, w.N, ea.dtype_code(w.dtype)),
+                     dtype=torch.uint8, device=dev)
+    o, lse = ea.fwd_unfused(qd, kd, vd, causal=w.causal, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    parity = None
+    if not args.no_check:
+        import oracle
+        rng = np.random.default_rng(1)
+        rows = np.unique(np.concatenate([np.arange(8), rng.integers(0, w.B * w.H * w.N, 56)]))
+        o_ref, _ = oracle.attn_fwd_ref_rows(q, k, v, w.causal, w.scale, rows)
+        parity = float(np.abs(o.cpu().double().numpy().reshape(-1, w.d)[rows] - o_ref).max())
+        if not parity <= (1e-4 if elem == 4 else 2e-2):
+            print(f"bench.py: unfused parity gate failed: {parity:.3e}", file=sys.stderr)
+            sys.exit(1)
+    steps = max(1, args.steps // 10)
+    ms_u, t_wall = _time_calls(lambda: ea.fwd_unfused(qd, kd, vd, causal=w.causal,
+                                                      scale=w.scale, workspace=ws),
+                               steps, max(1, args.warmup // 10))
+    out = (torch.empty_like(qd), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev))
+    ms_f, _ = _time_calls(lambda: ea.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=out),
+                          args.steps, args.warmup)
+    flops = attention_flops(w.B, w.H, w.N, w.d, w.causal)
+    tflops = flops / (ms_u * 1e-3) / 1e12
+    ld = (w.N + 63) // 64 * 64
+    # The method's own traffic: S written and read (fp32), P written and read
+    # (in the input type), plus Q, K, V read and O, lse written.
+    mbytes = (w.B * w.H * w.N * ld * (4 + 4 + 2 * elem)
+              + algorithmic_bytes(w.B, w.H, w.N, w.d, elem))
+    gbs = mbytes / (ms_u * 1e-3) / 1e9
+    line = {
+        "metric": "unfused attention fwd TFLOPS (S, softmax, P V as three kernels)",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(1, args.warmup // 10),
+        "ms_per_step": round(ms_u, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name,
+        "data": "synthetic (seeded i.i.d. N(0,1) inputs rounded to the dtype)",
+        "config": {"workload": w.describe() + " (unfused)", "name": name, "B": w.B, "H": w.H,
+                   "N": w.N, "d": w.d, "causal": w.causal, "scale": w.scale},
+        # The unfused path is bound by its N x N traffic.
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "fused_ms_per_step": round(ms_f, 5),
+        "fused_tflops": round(flops / (ms_f * 1e-3) / 1e12, 2),
+        "fusion_speedup": round(ms_u / ms_f, 2),
+        "parity_o_max_abs_sampled": parity,
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
 class _NoSmi(_Smi):
     def __init__(self):
         self.ok = False

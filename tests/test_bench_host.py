@@ -71,3 +71,28 @@ def test_limit_fractions():
     v1 = {"ticks": 300, "ppt_pwr": 110, "socket_thrm": 50}
     assert bench._Smi.limit_fracs(v0, v1) == {"ppt_pwr": 0.5, "socket_thrm": 0.25}
     assert bench._Smi.limit_fracs(v0, v0) is None
+
+
+def test_every_pass_has_its_runner():
+    """Each --pass of bench.py resolves to a function of the module (a run on
+    the GPU is the only other place that would notice a missing one)."""
+    for name in ("run_bwd", "run_unfused", "_time_calls", "median_launch_ms", "parity_stats",
+                 "cpu_baseline", "cpu_baseline_bwd", "device_state_under_load"):
+        assert callable(getattr(bench, name, None)), name
+    import ast
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    defined = set()
+    for n in ast.walk(tree):
+        if isinstance(n, (ast.FunctionDef, ast.ClassDef)):
+            defined.add(n.name)
+        elif isinstance(n, ast.Name) and isinstance(n.ctx, ast.Store):
+            defined.add(n.id)
+        elif isinstance(n, ast.arg):
+            defined.add(n.arg)
+        elif isinstance(n, ast.alias):
+            defined.add((n.asname or n.name).split(".")[0])
+    called = {n.func.id for n in ast.walk(tree)
+              if isinstance(n, ast.Call) and isinstance(n.func, ast.Name)}
+    import builtins
+    missing = {c for c in called if c not in defined and not hasattr(builtins, c)}
+    assert not missing, missing
