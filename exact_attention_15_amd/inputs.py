@@ -125,6 +125,12 @@ def make_structured_qkv(kind: str, B: int, H: int, N: int, d: int, dtype: torch.
       in the first tile and never moves afterwards.
     * ``"wide"``:    Q, K i.i.d. N(0, 4), scores with standard deviation ~4:
       rows are nearly one-hot and their maxima jump irregularly.
+    * ``"spikes"``:  q_i = u + 0.25 n, k_j = 0.25 n except three keys
+      j_s = (s + 1) N / 4 + 3 (s = 0, 1, 2), where k_j += 2.5 (s + 1) peak u
+      / sqrt(d): at the default scale their scores are about 2.5 (s + 1)
+      peak (100, 200, 300 at peak = 40), so a row's maximum jumps by more
+      than 128 log2 units inside one key tile, past what exp2 against the
+      old maximum can represent in fp32.
 
     V is i.i.d. N(0,1) in every case.
     """
@@ -142,6 +148,14 @@ def make_structured_qkv(kind: str, B: int, H: int, N: int, d: int, dtype: torch.
         ramp = (peak / N) * j / (d ** 0.5)
         k = ramp.view(1, 1, N, 1) * u + 0.25 * torch.randn((B, H, N, d), dtype=torch.float32,
                                                             generator=g)
+    elif kind == "spikes":
+        u = torch.randint(0, 2, (B, H, 1, d), generator=g).to(torch.float32) * 2.0 - 1.0
+        q = u + 0.25 * torch.randn((B, H, N, d), dtype=torch.float32, generator=g)
+        k = 0.25 * torch.randn((B, H, N, d), dtype=torch.float32, generator=g)
+        for s_ in range(3):
+            j = (s_ + 1) * N // 4 + 3
+            if j < N:
+                k[:, :, j, :] += (2.5 * (s_ + 1) * peak / d ** 0.5) * u[:, :, 0, :]
     else:
         raise ValueError(f"unknown kind {kind!r}")
     v = torch.randn((B, H, N, d), dtype=torch.float32, generator=g)

@@ -284,7 +284,7 @@ def _score_term(q, k, scale):
     return scale * (d + 2) * 2.0 ** -24 * m + 2.0 ** -20
 
 
-@pytest.mark.parametrize("kind", ["rising", "falling", "wide"])
+@pytest.mark.parametrize("kind", ["rising", "falling", "wide", "spikes"])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16],
                          ids=["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
@@ -293,8 +293,10 @@ def test_running_max_paths(ea, oracle_lib, kind, dtype, d, causal):
     """Score rows shaped to drive the online softmax's running maximum:
     rising rows move it by ~8 nats on every full 64-key tile (the accumulator
     is rescaled on every tile), falling rows fix it in the first tile, wide
-    rows (score std ~4) make it jump irregularly. N = 300 spans five key
-    tiles with a ragged tail."""
+    rows (score std ~4) make it jump irregularly, and spike rows make it
+    jump by ~100 nats inside one tile, so that the probabilities against the
+    old maximum overflow fp32 and the kernel must notice and redo the tile.
+    N = 300 spans five key tiles with a ragged tail."""
     n = 300
     q, k, v = make_structured_qkv(kind, 1, 2, n, d, dtype, seed=4100 + d)
     scale = ea.default_scale(d)

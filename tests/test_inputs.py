@@ -34,3 +34,8 @@ def test_structured_rows_have_the_intended_shape():
     q, k, _ = make_structured_qkv("wide", 1, 1, n, d, torch.float32, 7)
     s = q[0, 0].double() @ k[0, 0].double().T / d ** 0.5
     assert 3.0 < float(s.std()) < 5.0
+    # spikes at keys 78, 153, 228 (tiles 1, 2, 3): the last row's tile
+    # maxima climb by more than 128 log2 units from one tile to the next
+    spikes = _tile_maxima(*make_structured_qkv("spikes", 1, 1, n, d, torch.float32, 7)[:2], 5)
+    assert np.all(np.diff(spikes[:4]) > 128 * np.log(2)), spikes
+    assert abs(spikes[3] - 300.0) < 30.0 and spikes[4] < 10.0, spikes
