@@ -61,14 +61,15 @@
 //     exceeds it by more than 2^8 in probability; otherwise P <= 256 is used
 //     as is. The final O / l does not depend on the base, and a bf16/fp16 P
 //     keeps its relative precision at that magnitude.
-//   * At d = 64 with one query block the softmax step does not take the row
-//     maximum first: it exponentiates against the current base, then tests
-//     whether any packed P exceeds 2^8 (or overflowed) with 3-input packed
-//     16-bit maxima, eight per tile instead of ~25 instructions for the fp32
-//     maximum, its lane exchange and the comparison. Only if some row
-//     fails does the wave take the maximum and redo the tile against the
-//     moved base; the P it keeps is the same either way. The vector ALU is
-//     the busier unit there, so this is +4-5 % at the causal headline.
+//   * The softmax step does not take the row maximum first: it
+//     exponentiates against the current base, then tests whether any packed
+//     P exceeds 2^8 (or overflowed) with 3-input packed 16-bit maxima, eight
+//     per tile and query block instead of ~25 instructions for the fp32
+//     maximum, its lane exchange and the comparison. Only if some row fails
+//     does the wave take the maximum and redo the tile against the moved
+//     base; the P it keeps is the same either way. At d = 64 the vector ALU
+//     is the busier unit, so this is +4-5 % at the causal workloads and
+//     +5 % with two query blocks; at d = 128 it is +0-1 %.
 //   * The softmax row sum l runs on the matrix core as well: a 16x16x32
 //     MFMA with a constant 0/1 A operand sums the P operand of the P.V step
 //     over its keys (four per tile and query block), which takes ~60 fp32
@@ -319,15 +320,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
         for (int kb2 = 0; kb2 < 4; ++kb2) pk[qb][kb2] = u32x4{0u, 0u, 0u, 0u};
     }
 
-    // Row maxima and rescale decisions of the current tile. With two query
-    // blocks the VALU step is the longer of the two steps, so they are taken
-    // in the MFMA step (they need only S); with one block the MFMA step is
-    // the longer one and they stay in the VALU step (both measured).
-    constexpr bool kMaxInMfmaStep = QB == 2;
-    // Exponentials against the current base first, the row maximum only when
-    // a packed P exceeds 2^8 (d = 64, one query block: the vector ALU is the
-    // busier unit there).
-    constexpr bool kPackedCheck = D == 64 && QB == 1;
+    // Rescale decisions of the current tile (the row maxima are only taken
+    // when a tile's packed P fails the overflow test in the VALU step).
     float m_old[QB];
     bool need[QB];
     // Scores past the causal diagonal or past N become -inf.
@@ -365,10 +359,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
             need[qb] = mx > m_old[qb] + kRescaleThreshold;
             m_used[qb] = need[qb] ? mx : m_old[qb];
         }
-    };
-    auto mask_and_max = [&](int jj) __attribute__((always_inline)) {
-        mask_tile(jj);
-        row_max_need();
     };
 
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this lane's copy of K(0)
@@ -496,9 +486,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
                 __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 2);
             }
         }
-        // (jj < n_tiles is implied by jj < n_live; stated, it lets the
-        // compiler drop this from the last step, whose S is never used.)
-        if (kMaxInMfmaStep && jj < n_tiles && jj < n_live) mask_and_max(jj);
     };
 
     // VALU step of tile jj: online softmax of S(jj) into P for every query
@@ -520,49 +507,52 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
             }
             return;
         }
-        if constexpr (kPackedCheck) {
-            mask_tile(jj);
-            if (jj > 0) {
-                // Past tile 0 every row's base is finite (each row sees key
-                // 0 there). P against it, keeping S for the rare case below.
-                const float m_sub = m_used[0];
+        mask_tile(jj);
+        if (jj > 0) {
+            // Past tile 0 every row's base is finite (each row sees key 0
+            // there): P against it, keeping S for the rare case below, and
+            // the lane's largest packed P. P >= 0, and non-negative 16-bit
+            // floats order as their bit patterns do, so bf16 values read as
+            // fp16 keep their order up to ~2^121; beyond that they read as
+            // inf or NaN, which the test below also catches (as it catches
+            // an overflowed P, inf or NaN).
+            uint32_t c = 0u;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float m_sub = m_used[qb];
 #pragma unroll
                 for (int kb2 = 0; kb2 < 4; ++kb2)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 8 * (kb2 & 1) + 2 * e;
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[0][kb2 >> 1][i], c2, -m_sub));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[0][kb2 >> 1][i + 1], c2, -m_sub));
-                        pk[0][kb2][e] = Op::pack2(p0, p1);
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb2 >> 1][i], c2, -m_sub));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb2 >> 1][i + 1], c2, -m_sub));
+                        pk[qb][kb2][e] = Op::pack2(p0, p1);
                     }
-                // Largest packed P of the lane. P >= 0, and non-negative
-                // 16-bit floats order as their bit patterns do, so bf16
-                // values read as fp16 keep their order up to ~2^121; beyond
-                // that they read as inf or NaN, which the test below also
-                // catches (as it catches an overflowed P, inf or NaN).
-                uint32_t c = pk_max3_f16(pk[0][0][0], pk[0][0][1], pk[0][0][2]);
-                c = pk_max3_f16(c, pk[0][0][3], pk[0][1][0]);
-                c = pk_max3_f16(c, pk[0][1][1], pk[0][1][2]);
-                c = pk_max3_f16(c, pk[0][1][3], pk[0][2][0]);
-                c = pk_max3_f16(c, pk[0][2][1], pk[0][2][2]);
-                c = pk_max3_f16(c, pk[0][2][3], pk[0][3][0]);
-                c = pk_max3_f16(c, pk[0][3][1], pk[0][3][2]);
-                c = pk_max3_f16(c, pk[0][3][3], pk[0][3][3]);
-                // 2^8 as a packed value read as fp16 (bf16 0x4380 reads 3.75).
-                const _Float16 lim = IS_BF16 ? (_Float16)3.75f : (_Float16)256.0f;
-                const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(c & 0xffffu));
-                const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(c >> 16));
-                const bool over = !(lo <= lim) || !(hi <= lim);
-                if (__builtin_amdgcn_ballot_w64(over) == 0) {
-                    need[0] = false;   // P <= 2^8 everywhere: the base stays
-                    return;
-                }
+                uint32_t cq = pk_max3_f16(pk[qb][0][0], pk[qb][0][1], pk[qb][0][2]);
+                cq = pk_max3_f16(cq, pk[qb][0][3], pk[qb][1][0]);
+                cq = pk_max3_f16(cq, pk[qb][1][1], pk[qb][1][2]);
+                cq = pk_max3_f16(cq, pk[qb][1][3], pk[qb][2][0]);
+                cq = pk_max3_f16(cq, pk[qb][2][1], pk[qb][2][2]);
+                cq = pk_max3_f16(cq, pk[qb][2][3], pk[qb][3][0]);
+                cq = pk_max3_f16(cq, pk[qb][3][1], pk[qb][3][2]);
+                cq = pk_max3_f16(cq, pk[qb][3][3], pk[qb][3][3]);
+                c = qb == 0 ? cq : pk_max3_f16(c, cq, cq);
             }
-            // Tile 0, or some P above 2^8: the exact rule below, on S.
-            row_max_need();
-        } else if (!kMaxInMfmaStep) {
-            mask_and_max(jj);
+            // 2^8 as a packed value read as fp16 (bf16 0x4380 reads 3.75).
+            const _Float16 lim = IS_BF16 ? (_Float16)3.75f : (_Float16)256.0f;
+            const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(c & 0xffffu));
+            const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(c >> 16));
+            const bool over = !(lo <= lim) || !(hi <= lim);
+            if (__builtin_amdgcn_ballot_w64(over) == 0) {
+                // P <= 2^8 everywhere: every base stays.
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) need[qb] = false;
+                return;
+            }
         }
+        // Tile 0, or some P above 2^8: the exact rule, on S.
+        row_max_need();
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             // The base is -inf only while every score so far is masked, which

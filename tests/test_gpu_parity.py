@@ -234,6 +234,29 @@ def test_long_sequence(ea, oracle_lib, dtype, d, n, causal):
            f"N={n} d={d} {dtype} causal={causal} ({len(rows)} sampled rows)", n)
 
 
+@pytest.mark.parametrize("kind", ["rising", "spikes"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_two_query_block_running_max(ea, oracle_lib, kind, dtype):
+    """The two-query-block kernel (non-causal, d = 64, 512-row items on
+    every compute unit: 128 slices x 2 tiles) on score rows whose maximum
+    moves on every key tile (rising) or jumps past fp32's exp2 range inside
+    one tile (spikes): sampled rows, the first and last included, against
+    the oracle."""
+    B, H, n, d = 1, 128, 1000, 64
+    q, k, v = make_structured_qkv(kind, B, H, n, d, dtype, seed=5300)
+    scale = ea.default_scale(d)
+    o, lse = _run_gpu(ea, q, k, v, False, scale)
+    rows = _sample_rows(B, H, n, np.random.default_rng(5300), n_random=96)
+    o_ref, lse_ref = oracle_lib.attn_fwd_ref_rows(q, k, v, False, scale, rows)
+    err_o = float(np.abs(o.reshape(-1, d)[rows] - o_ref).max())
+    err_l = float(np.abs(lse.reshape(-1)[rows] - lse_ref).max())
+    tol_l = lse_tol(dtype, n) + _score_term(q, k, scale)
+    print(f"two query blocks {kind} {dtype} ({len(rows)} sampled rows): O max-abs {err_o:.3e}, "
+          f"lse max-abs {err_l:.3e} (bound {tol_l:.3e})", flush=True)
+    assert np.all(np.isfinite(o)) and err_o <= O_TOL[dtype], err_o
+    assert err_l <= tol_l, err_l
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],
                          ids=["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
