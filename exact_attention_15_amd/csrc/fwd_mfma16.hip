@@ -489,11 +489,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
     };
 
     // VALU step of tile jj: online softmax of S(jj) into P for every query
-    // block, and the rescale of O where the exponent base moved. The blocks'
-    // maxima, exponentials and packing form one straight stretch of code (the
-    // rescale branches come last), so the compiler can overlap one block's
-    // maximum with the other block's exponentials: v_exp_f32, one per ~23
-    // cycles of a wave, is what bounds this step.
+    // block, and the rescale of O where the exponent base moved. In the
+    // common case (no P above 2^8) it is one straight stretch of fma, exp2,
+    // pack and packed maxima; the row maxima and the rescale branches only
+    // run on tile 0 and where a base moves.
     auto valu_step = [&](int jj) __attribute__((always_inline)) {
         if (jj >= n_live) {
             // Past this wave's rows: no P. At d = 64 with one query block,
