@@ -364,11 +364,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this lane's copy of K(0)
     __syncthreads();
 
-    // MFMA step of tile jj: S(jj) = K(jj) Q^T, and O += P(jj-1) V(jj-1) when
-    // HAS_PV. K(jj) sits in k_lds[jj&1], V(jj-1) in v_lds[(jj-1)&1]: KPAR = jj&1.
-    auto mfma_step = [&](int jj, auto kpar_tag, auto has_pv_tag) __attribute__((always_inline)) {
+    // MFMA step of tile jj: S(jj) = K(jj) Q^T when HAS_S, and O += P(jj-1)
+    // V(jj-1) when HAS_PV. K(jj) sits in k_lds[jj&1], V(jj-1) in
+    // v_lds[(jj-1)&1]: KPAR = jj&1.
+    auto mfma_step = [&](int jj, auto kpar_tag, auto has_pv_tag, auto has_s_tag) __attribute__((always_inline)) {
         constexpr int KPAR = decltype(kpar_tag)::value;
         constexpr bool HAS_PV = decltype(has_pv_tag)::value;
+        constexpr bool HAS_S = decltype(has_s_tag)::value;
         const LDS_AS char* kb_base = (const LDS_AS char*)(KPAR ? k_lds1 : k_lds0);
         const LDS_AS char* vb_base = (const LDS_AS char*)(KPAR ? v_lds0 : v_lds1);
         if constexpr (D == 64 && QB == 1) {
@@ -406,9 +408,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
                 __builtin_amdgcn_sched_group_barrier(0x008, PF, 2);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // S for every tile, also ones past this wave's rows (never read).
-            // The two key blocks' products alternate: consecutive MFMAs
-            // share their Q operand.
+            if constexpr (HAS_S) {
 #pragma unroll
             for (int kd = 0; kd < NKD; ++kd)
 #pragma unroll
@@ -425,13 +425,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
             }
             __builtin_amdgcn_sched_group_barrier(0x008, KF, 3);
             __builtin_amdgcn_sched_barrier(0);
+            }
         } else {
-            // S is computed for every tile, also ones this wave does not need
-            // (their S is never read): a conditional S would cost register copies.
             // The two key blocks' products alternate, so that consecutive MFMAs
             // share their Q operand (each accumulator still sums over d in
             // order): fewer operand bits toggle, and under the power limit that
             // is clock (+0.5 % at d = 128 and at fp16 N = 16k).
+            if constexpr (HAS_S) {
     #pragma unroll
             for (int kd = 0; kd < NKD; ++kd)
     #pragma unroll
@@ -441,8 +441,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
                     for (int qb = 0; qb < QB; ++qb)
                         s[qb][kb] = Op::mfma(a, qf[qb][kd], kd == 0 ? f32x16{} : s[qb][kb]);
                 }
+            }
             // Order: three K fragment reads ahead, then one more read per QB
             // MFMAs, so that LDS latency hides behind the matrix core.
+            if constexpr (HAS_S) {
             constexpr int kSReads = 2 * NKD;
             __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);
     #pragma unroll
@@ -451,10 +453,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 3 * QB, 1);
+            }
             // Keeps the P.V operand reads from being hoisted over the S products
             // (more live registers than the wave has).
             __builtin_amdgcn_sched_barrier(0);
-            // P of a tile past this wave's rows is all zero, so its P.V is skipped.
+            // No P.V for a tile past this wave's rows (no P was made for it).
             if (HAS_PV && jj - 1 < n_live) {
     #pragma unroll
                 for (int kb2 = 0; kb2 < 4; ++kb2)
@@ -494,18 +497,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
     // pack and packed maxima; the row maxima and the rescale branches only
     // run on tile 0 and where a base moves.
     auto valu_step = [&](int jj) __attribute__((always_inline)) {
-        if (jj >= n_live) {
-            // Past this wave's rows: no P. At d = 64 with one query block,
-            // defining the P registers anyway ends the previous P's life at
-            // the P.V products that read it (otherwise the compiler keeps it
-            // across the next S products), which frees them for the K
-            // fragments read ahead there.
-            if constexpr (D == 64 && QB == 1) {
-#pragma unroll
-                for (int kb2 = 0; kb2 < 4; ++kb2) pk[0][kb2] = u32x4{0u, 0u, 0u, 0u};
-            }
-            return;
-        }
+        // (Tiles past this wave's rows go to dead_steps and do not get here;
+        // the check is kept for the register allocation it leads to: without
+        // it the two-block kernel takes two more VGPRs.)
+        if (jj >= n_live) return;
         mask_tile(jj);
         if (jj > 0) {
             // Past tile 0 every row's base is finite (each row sees key 0
@@ -612,7 +607,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
     auto tile_steps = [&](int j, auto par_tag, auto has_pv_tag) __attribute__((always_inline)) {
         copies(j, par_tag);
         ATTN_PROBE(j);
-        mfma_step(j, par_tag, has_pv_tag);
+        mfma_step(j, par_tag, has_pv_tag, std::true_type{});
         ATTN_PROBE(j + 1);
         barrier();
         valu_step(j);
@@ -626,18 +621,49 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
     using NoPV = std::integral_constant<bool, false>;
     using WithPV = std::integral_constant<bool, true>;
 
+    // Under a causal mask the tiles n_live .. n_tiles-1 are dead for this
+    // wave: it only takes part in their copies and barriers (every wave of
+    // the workgroup passes the same 2 n_tiles + 1 barriers), and the first
+    // of them still holds the P.V products of tile n_live-1. Leaving out
+    // their S products (which a branch inside the MFMA step could only do
+    // with register copies and spills) is +1.2-1.4 % on the causal
+    // workloads.
+    auto dead_steps = [&](int j, auto par_tag, auto first_tag) __attribute__((always_inline)) {
+        copies(j, par_tag);
+        ATTN_PROBE(j);
+        if constexpr (decltype(first_tag)::value) mfma_step(j, par_tag, std::true_type{}, std::false_type{});
+        ATTN_PROBE(j + 1);
+        barrier();
+        if (grp == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+        ATTN_PROBE(j + 2);
+        barrier();
+    };
+
     // Group B runs one step behind group A.
     if (grp == 1) barrier();
     tile_steps(0, P0{}, NoPV{});
     int j = 1;
-    for (; j + 1 < n_tiles; j += 2) {
+    // (Without a mask n_live is n_tiles.)
+    const int n_loop = CAUSAL ? n_live : n_tiles;
+    for (; j + 1 < n_loop; j += 2) {
         tile_steps(j, P1{}, WithPV{});
         tile_steps(j + 1, P0{}, WithPV{});
     }
-    if (j < n_tiles) tile_steps(j, P1{}, WithPV{});
-    // Final P.V of tile n_tiles-1 (the S computed alongside is unused).
-    if (n_tiles & 1) mfma_step(n_tiles, P1{}, WithPV{});
-    else mfma_step(n_tiles, P0{}, WithPV{});
+    if (j < n_loop) tile_steps(j, P1{}, WithPV{});
+    if constexpr (CAUSAL) {
+        j = n_live;
+        if (j < n_tiles) {
+            if (j & 1) dead_steps(j, P1{}, std::true_type{});
+            else dead_steps(j, P0{}, std::true_type{});
+            for (++j; j < n_tiles; ++j) {
+                if (j & 1) dead_steps(j, P1{}, std::false_type{});
+                else dead_steps(j, P0{}, std::false_type{});
+            }
+        }
+    }
+    // Final P.V of tile n_tiles-1 when it is live for this wave (no S).
+    if (n_tiles & 1) mfma_step(n_tiles, P1{}, WithPV{}, std::false_type{});
+    else mfma_step(n_tiles, P0{}, WithPV{}, std::false_type{});
     if (grp == 0) barrier();
 
     // Epilogue: O = O~ / l, rounded once to the output type; lse in fp32.
