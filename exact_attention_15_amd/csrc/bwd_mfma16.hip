@@ -199,6 +199,12 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, GROUPS == 3 ? 3 : 2) void bwd
             vf[kd] = *(const u32x4*)(vr + 16 * kd);
         }
     }
+    // vmcnt(0): the fragments are in. Without this wait the compiler places
+    // its waits for them at their first use inside the query loop, where
+    // every step then also waits for the next stage's copies in flight
+    // (they count in the same counter): vmcnt(0) in the middle of each
+    // 32-query block.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
 
     int roff[NKD];   // row reads: row l32 (+32 qb), logical chunk 2kd + g
 #pragma unroll
