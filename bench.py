@@ -651,8 +651,12 @@ def main():
     traffic = measured_traffic(name)
     lf = dev_state["limit_fracs"] or {}
 
+    # The headline workload carries the headline metric's name; the others
+    # the same measure, named for their own dtype (config names the shape).
+    metric = ("attention fwd TFLOPS (bf16, causal, N=4096 d=64); % of MFMA peak" if name == HEADLINE
+              else f"attention fwd TFLOPS ({dt_name}); % of MFMA peak")
     line = {
-        "metric": "attention fwd TFLOPS (bf16, causal, N=4096 d=64); % of MFMA peak",
+        "metric": metric,
         "value": round(tflops, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
