@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
         const LDS_AS char* kb_base = (const LDS_AS char*)(KPAR ? k_lds1 : k_lds0);
         const LDS_AS char* vb_base = (const LDS_AS char*)(KPAR ? v_lds0 : v_lds1);
         if constexpr (D == 64 && QB == 1) {
-            // P.V of the previous tile first, then S. At 126 registers the
+            // P.V of the previous tile first, then S. At ~128 registers the
             // wave has no spare ones to read operands ahead, but the S
             // accumulators are dead until the S products (their last values
             // became P in the softmax step) and P is dead after the P.V
