@@ -73,11 +73,24 @@ def _configure(lib):
     lib.attn_unfused_workspace_bytes.restype = i64
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_debug_set_fwd_variant.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.attn_debug_set_fwd_variant.restype = ctypes.c_int
     return lib
 
 
 def strerror(code: int) -> str:
     return load_library().attn_strerror(int(code)).decode()
+
+
+def debug_set_fwd_variant(query_blocks: int = 0, order: int = 0) -> None:
+    """Debugging and testing only: force the 16-bit forward's query blocks
+    per wave (0 automatic, 1, 2) and work order (0 automatic, 1 tile-major,
+    2 XCD-major) for every later call in the process; outputs are
+    bit-identical across variants. `debug_set_fwd_variant()` restores the
+    automatic choice."""
+    rc = load_library().attn_debug_set_fwd_variant(int(query_blocks), int(order))
+    if rc != ATTN_OK:
+        raise AttnError(rc, strerror(rc), "attn_debug_set_fwd_variant")
 
 
 def dtype_code(dtype) -> int:
@@ -268,5 +281,5 @@ def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, works
     return o, lse
 
 
-__all__ = ["fwd", "bwd", "fwd_unfused", "attn_fwd_unfused", "unfused_workspace_bytes", "attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
+__all__ = ["fwd", "bwd", "debug_set_fwd_variant", "fwd_unfused", "attn_fwd_unfused", "unfused_workspace_bytes", "attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
            "dtype_code", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -8,6 +8,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/attn.h"
@@ -49,6 +50,10 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
     return mis != 0 ? ATTN_EALIGN : ATTN_OK;
 }
 
+// Variant overrides of attn_debug_set_fwd_variant (0: automatic).
+std::atomic<int> g_force_qb{0};
+std::atomic<int> g_force_order{0};
+
 }  // namespace
 
 extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -70,6 +75,8 @@ extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o
     p.G = (int)(H / H_kv);
     p.n_qtiles = 0;    // set by the launcher for its own query tile
     p.xcd_order = 0;   // chosen by the launcher
+    p.force_qb = g_force_qb.load(std::memory_order_relaxed);
+    p.force_order = g_force_order.load(std::memory_order_relaxed);
     // scale * log2(e), rounded once to fp32: scores go straight into exp2.
     p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
 
@@ -225,6 +232,13 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                         int dtype, void* stream) {
     return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
+}
+
+extern "C" int attn_debug_set_fwd_variant(int query_blocks, int order) {
+    if (query_blocks < 0 || query_blocks > 2 || order < 0 || order > 2) return ATTN_EINVAL;
+    g_force_qb.store(query_blocks, std::memory_order_relaxed);
+    g_force_order.store(order, std::memory_order_relaxed);
+    return ATTN_OK;
 }
 
 extern "C" const char* attn_strerror(int code) {

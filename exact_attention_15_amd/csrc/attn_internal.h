@@ -20,6 +20,8 @@ struct FwdParams {
     int G;              // H / H_kv query heads per key/value head
     int n_qtiles;       // ceil(N / query-tile rows)
     int xcd_order;      // 1: XCD-major work order (fwd_order.h), 0: tile-major
+    int force_qb;       // 0 automatic, 1 or 2 query blocks (attn_debug_set_fwd_variant)
+    int force_order;    // 0 automatic, 1 tile-major, 2 XCD-major
     float scale_log2;   // scale * log2(e): scores enter exp2 directly
 };
 

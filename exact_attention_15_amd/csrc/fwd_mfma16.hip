@@ -699,6 +699,8 @@ hipError_t launch_qb(FwdParams p, hipStream_t s) {
     // round (long and short items sharing compute units): 22 % slower at
     // B4 H16 N4096 d64, so those grids stay tile-major.
     p.xcd_order = (!CAUSAL && fwdorder::xcd_major_applies(p.BH_kv)) ? 1 : 0;
+    if (p.force_order == 1) p.xcd_order = 0;
+    if (p.force_order == 2 && fwdorder::xcd_major_applies(p.BH_kv)) p.xcd_order = 1;
     const dim3 grid((unsigned)(p.n_qtiles * p.BH));
     hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL, QB>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
@@ -713,7 +715,8 @@ template <bool IS_BF16, int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t s) {
     if constexpr (D == 64 && !CAUSAL) {
         const int64_t items2 = (p.N + block_m<2>() - 1) / block_m<2>() * p.BH;
-        if (items2 >= kComputeUnits) return launch_qb<IS_BF16, D, CAUSAL, 2>(p, s);
+        const bool two = p.force_qb == 0 ? items2 >= kComputeUnits : p.force_qb == 2;
+        if (two) return launch_qb<IS_BF16, D, CAUSAL, 2>(p, s);
     }
     return launch_qb<IS_BF16, D, CAUSAL, 1>(p, s);
 }

@@ -203,6 +203,29 @@ int64_t attn_unfused_workspace_bytes(int64_t B, int64_t H, int64_t N, int dtype)
 /* attn_strerror — static description of a return code (never NULL). */
 const char* attn_strerror(int code);
 
+/*
+ * attn_debug_set_fwd_variant — debugging and testing only: force the
+ * variant that attn_fwd / attn_fwd_gqa choose per call for fp16 and bf16
+ * inputs, for every later call from any thread of the process (a call
+ * already being launched on another thread may or may not see it).
+ *
+ *   query_blocks  0: automatic; 1: one 32-row query block per wave (256-row
+ *                 work items); 2: two blocks per wave (512-row items), which
+ *                 only the d = 64 non-causal kernel has: elsewhere 2 acts as
+ *                 0.
+ *   order         0: automatic; 1: tile-major work order (longest query
+ *                 tiles first, consecutive items on different slices);
+ *                 2: XCD-major (each of the 8 XCDs takes its K/V slices one
+ *                 after another), applied only when B*H_kv is a multiple of
+ *                 8, elsewhere 2 acts as 0.
+ *
+ * Every variant computes each output row with the same arithmetic in the
+ * same order, so outputs are bit-identical across variants; only the work
+ * decomposition and the speed change. Returns ATTN_OK, or ATTN_EINVAL (and
+ * changes nothing) for a value outside the ranges above. Makes no HIP call.
+ */
+int attn_debug_set_fwd_variant(int query_blocks, int order);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,8 +45,9 @@ def test_every_header_is_covered():
 
 def test_attn_library_exports_header(attn_lib_path):
     decl = _declared_functions("attn.h")
-    assert decl == ["attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_gqa", "attn_fwd_unfused",
-                    "attn_strerror", "attn_unfused_workspace_bytes"]
+    assert decl == ["attn_bwd", "attn_bwd_noalloc", "attn_debug_set_fwd_variant", "attn_fwd",
+                    "attn_fwd_gqa", "attn_fwd_unfused", "attn_strerror",
+                    "attn_unfused_workspace_bytes"]
     missing = set(decl) - _exported(attn_lib_path)
     assert not missing, missing
     ctypes.CDLL(attn_lib_path)   # loads without a GPU
@@ -80,6 +81,21 @@ def test_libraries_share_no_symbols(attn_lib_path, oracle_lib):
     needed = subprocess.run(["readelf", "-d", attn_lib_path], check=True,
                             capture_output=True, text=True).stdout
     assert "oracle" not in needed
+
+
+def test_debug_variant_switch(attn_lib_path):
+    """attn_debug_set_fwd_variant takes 0..2 for each argument (no HIP
+    call), rejects anything else without changing the setting, and the
+    automatic choice can always be restored."""
+    import exact_attention_15_amd as ea
+    lib = ea.load_library()
+    for qb, order in ((0, 0), (1, 2), (2, 1), (0, 0)):
+        assert lib.attn_debug_set_fwd_variant(qb, order) == ea.ATTN_OK
+    for qb, order in ((3, 0), (-1, 0), (0, 3), (0, -1)):
+        assert lib.attn_debug_set_fwd_variant(qb, order) == ea.ATTN_EINVAL
+    with pytest.raises(ea.AttnError):
+        ea.debug_set_fwd_variant(5, 0)
+    ea.debug_set_fwd_variant()
 
 
 def test_strerror(attn_lib_path):

@@ -257,6 +257,38 @@ def test_two_query_block_running_max(ea, oracle_lib, kind, dtype):
     assert err_l <= tol_l, err_l
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_forced_variants_are_bit_identical(ea, dtype):
+    """Every forward variant computes each row with the same arithmetic in
+    the same order: forcing one or two query blocks per wave, or the
+    tile-major or XCD-major work order (attn_debug_set_fwd_variant), gives
+    the automatic choice's output bit for bit, on shapes where the
+    automatic choice is the other variant: d = 64 non-causal with 256
+    512-row items (automatic: two blocks, XCD-major), a small non-causal
+    shape (one block), and causal shapes with 8 K/V slices (tile-major),
+    multi-head and grouped-query."""
+    cases = [(2, 64, 64, 1000, 64, False, [(1, 0), (0, 1), (1, 1)]),
+             (1, 2, 2, 300, 64, False, [(2, 0)]),
+             (1, 8, 8, 700, 64, True, [(0, 2), (2, 2)]),
+             (2, 16, 4, 640, 64, True, [(0, 2)]),
+             (1, 8, 8, 520, 128, False, [(0, 1), (2, 1)]),
+             (1, 8, 8, 520, 128, True, [(0, 2)])]
+    try:
+        for B, H, H_kv, n, d, causal, forced in cases:
+            q, k, v = (t.cuda() for t in make_qkv(B, H, n, d, dtype, seed=8800 + n, H_kv=H_kv))
+            ea.debug_set_fwd_variant()
+            o_auto, lse_auto = ea.fwd(q, k, v, causal=causal)
+            for qb, order in forced:
+                ea.debug_set_fwd_variant(qb, order)
+                o, lse = ea.fwd(q, k, v, causal=causal)
+                torch.cuda.synchronize()
+                print(f"B{B} H{H}/{H_kv} N{n} d{d} causal={causal} forced (qb={qb}, order={order}): "
+                      f"identical={torch.equal(o, o_auto) and torch.equal(lse, lse_auto)}", flush=True)
+                assert torch.equal(o, o_auto) and torch.equal(lse, lse_auto), (B, H, n, d, causal, qb, order)
+    finally:
+        ea.debug_set_fwd_variant()
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],
                          ids=["f32", "bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
