@@ -135,6 +135,8 @@ int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* ls
  *              fp32; for f16/bf16, p and ds are rounded to `dtype` as the
  *              operands of the dv, dk and dq products and outputs are rounded
  *              once (nearest even) from fp32; fp32 rounds nothing below fp32.
+ *              p comes from the hardware exp2, which has no subnormal
+ *              results: every p below 2^-126 is taken as 0 (all dtypes).
  * stream       hipStream_t (NULL = the null stream).
  *
  * Asynchronous: three kernels (four when the f16/bf16 dk/dv work of

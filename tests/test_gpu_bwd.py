@@ -23,8 +23,8 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_15_amd.inputs import WORKLOADS, make_dout, make_qkv, workload_dout, \
-    workload_inputs
+from exact_attention_15_amd.inputs import WORKLOADS, make_dout, make_qkv, make_structured_qkv, \
+    workload_dout, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -56,11 +56,32 @@ def _score_term(q, k, scale):
     return q.shape[-1] * 2.0 ** -24 * float(scale) * m + 2.0 ** -22
 
 
-def _check(got, ref, err, zerr, dtype, n_acc, what, u_s):
+def _flush_terms(q, k, v, dout, scale):
+    """Absolute error that the kernels' exp2 adds by returning 0 for every p
+    below 2^-126 (the hardware instruction has no subnormal results): a lost
+    p_ij moves ds_ij = p_ij (dp_ij - D_i) by at most 2^-126 |dO_i|_1 2 max|v|
+    (|dp_ij| and |D_i| are each at most |dO_i|_1 max|v|, o_i being a convex
+    combination of the rows of v) and dv_j by 2^-126 |dO_ic|. Summed over
+    every row and key, masked or not, so an upper bound under a causal mask
+    too. Returns (fq, fk, fv) shaped like dq, dk, dv."""
+    G = q.shape[1] // k.shape[1]
+    qa, ka, da = (t.to(torch.float64).abs() for t in (q, k, dout))
+    g = da.sum(-1, keepdim=True)                                   # [B,H,N,1]
+    c = 2.0 ** -126 * 2.0 * float(v.to(torch.float64).abs().max()) * float(scale)
+    ksum = ka.sum(2, keepdim=True).repeat_interleave(G, dim=1)     # [B,H,1,d]
+    fq = c * g * ksum
+    B, H, N, d = q.shape
+    fk = c * (g * qa).sum(2, keepdim=True).reshape(B, H // G, G, 1, d).sum(2)
+    fv = 2.0 ** -126 * da.sum(2, keepdim=True).reshape(B, H // G, G, 1, d).sum(2)
+    return tuple(np.broadcast_to(t.numpy(), s) for t, s in
+                 ((fq, q.shape), (fk, k.shape), (fv, v.shape)))
+
+
+def _check(got, ref, err, zerr, dtype, n_acc, what, u_s, flush=0.0):
     got = got.to(torch.float64).cpu().numpy() if isinstance(got, torch.Tensor) else got
     assert np.all(np.isfinite(got)), what
     bound = 2 * ((U[dtype] + u_s + n_acc * 2.0 ** -24) * (err + np.abs(ref)) +
-                 SUB[dtype] / 2 * (zerr + 1))
+                 SUB[dtype] / 2 * (zerr + 1) + flush)
     diff = np.abs(got - ref)
     ratio = float((diff / np.maximum(bound, 1e-300)).max())
     print(f"{what}: max-abs {float(diff.max()):.3e}, max err/bound {ratio:.3f}", flush=True)
@@ -75,9 +96,10 @@ def _bwd_and_check(ea, oracle_lib, q, k, v, dout, causal, scale, what):
                                                                  error_scales=True)
     n_acc = (q.shape[1] // k.shape[1]) * q.shape[2] / 16 + 32
     u_s = _score_term(q, k, scale)
-    _check(dq, rq, eq, zq, q.dtype, n_acc, what + " dq", u_s)
-    _check(dk, rk, ek, zk, q.dtype, n_acc, what + " dk", u_s)
-    _check(dv, rv, ev, zv, q.dtype, n_acc, what + " dv", u_s)
+    fq, fk, fv = _flush_terms(q, k, v, dout, scale)
+    _check(dq, rq, eq, zq, q.dtype, n_acc, what + " dq", u_s, fq)
+    _check(dk, rk, ek, zk, q.dtype, n_acc, what + " dk", u_s, fk)
+    _check(dv, rv, ev, zv, q.dtype, n_acc, what + " dv", u_s, fv)
 
 
 SWEEP = [(1, 2, 2), (2, 4, 1), (17, 2, 2), (64, 4, 2), (65, 2, 2), (127, 6, 3), (128, 2, 2),
@@ -102,6 +124,22 @@ def test_bwd_sweep_small(ea, oracle_lib, dtype, d, causal):
         dout = make_dout(2, H, n, d, dtype, seed=seed)
         _bwd_and_check(ea, oracle_lib, q, k, v, dout, causal, ea.default_scale(d),
                        f"N={n} H={H} H_kv={H_kv} d={d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("kind", ["rising", "wide", "spikes"])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32],
+                         ids=["f16", "bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bwd_structured_scores(ea, oracle_lib, kind, dtype, causal):
+    """The backward on the forward's running-maximum inputs: rows whose
+    scores climb across key tiles, rows nearly one-hot (score std ~4), and
+    rows with keys ~100, 200 and 300 nats above the rest (p exactly 0 or 1
+    for most entries, lse dominated by one key). Every element against the
+    oracle, N = 300 (five key tiles, ragged)."""
+    q, k, v = make_structured_qkv(kind, 1, 2, 300, 64, dtype, seed=9900)
+    dout = make_dout(1, 2, 300, 64, dtype, seed=9900)
+    _bwd_and_check(ea, oracle_lib, q, k, v, dout, causal, ea.default_scale(64),
+                   f"{kind} N=300 d=64 {dtype} causal={causal}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -170,9 +208,10 @@ def test_bwd_workload_full_size(ea, oracle_lib, name):
         hs = slice(hk * G, (hk + 1) * G)
         tag = f"{name} slice b={b} h_kv={hk}"
         u_s = _score_term(sub[0], sub[1], w.scale)
-        _check(dq[b:b + 1, hs], rq, eq, zq, w.dtype, n_acc, tag + " dq", u_s)
-        _check(dk[b:b + 1, hk:hk + 1], rk, ek, zk, w.dtype, n_acc, tag + " dk", u_s)
-        _check(dv[b:b + 1, hk:hk + 1], rv, ev, zv, w.dtype, n_acc, tag + " dv", u_s)
+        fq, fk, fv = _flush_terms(*sub, w.scale)
+        _check(dq[b:b + 1, hs], rq, eq, zq, w.dtype, n_acc, tag + " dq", u_s, fq)
+        _check(dk[b:b + 1, hk:hk + 1], rk, ek, zk, w.dtype, n_acc, tag + " dk", u_s, fk)
+        _check(dv[b:b + 1, hk:hk + 1], rv, ev, zv, w.dtype, n_acc, tag + " dv", u_s, fv)
     # Identities on every slice: the keys' gradients sum to zero over keys;
     # the values' gradients sum to the group's summed dout.
     dk64 = dk.to(torch.float64)
