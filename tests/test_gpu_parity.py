@@ -9,7 +9,9 @@ after rounding them to the P.V operand type, whose rounding error is at most
 u|p| + s/2 (unit roundoff u = 2^-8 bf16, 2^-11 fp16; subnormal spacing
 s = 2^-24 fp16, 2^-133 bf16). The largest probability of a row is >= 1, so
 l >= 1 and ln(l) moves by at most u + N s/2; the fp32 row sum adds one
-rounding per accumulator update, and 1e-5 covers the fp32 scores.
+rounding per accumulator update, and 1e-5 covers the fp32 scores and the
+hardware exp2's zero for every p below 2^-126 (no subnormal results: at most
+N 2^-126 more).
 
 Small shapes are checked element by element on every output; the full-size
 workloads (in the launch configuration the bench times) on every row, or on
