@@ -96,6 +96,29 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
     return tuple(out)
 
 
+def make_qkv_device(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
+                    H_kv: int | None = None, device: str = "cuda"):
+    """Like ``make_qkv`` (i.i.d. N(0,1) float32, rounded to the dtype; Q, then
+    K and V) but drawn by the device's generator seeded with ``seed``, for
+    tensors too large to draw on the host. Other bits than ``make_qkv``'s;
+    a test copies the slices it checks to the host for the oracle."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    kv = H if H_kv is None else H_kv
+    return tuple(torch.randn((B, heads, N, d), dtype=torch.float32, device=device,
+                             generator=g).to(dtype)
+                 for heads in (H, kv, kv))
+
+
+def make_dout_device(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
+                     device: str = "cuda"):
+    """The incoming gradient drawn on the device (seed + 10**6)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) + 10 ** 6)
+    return torch.randn((B, H, N, d), dtype=torch.float32, device=device,
+                       generator=g).to(dtype)
+
+
 def make_dout(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int):
     """The incoming gradient of O for the backward pass: i.i.d. N(0,1) fp32
     from its own generator (seed + 10**6), rounded to the dtype."""

@@ -23,8 +23,8 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_15_amd.inputs import WORKLOADS, make_dout, make_qkv, make_structured_qkv, \
-    workload_dout, workload_inputs
+from exact_attention_15_amd.inputs import WORKLOADS, make_dout, make_dout_device, make_qkv, \
+    make_qkv_device, make_structured_qkv, workload_dout, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -249,6 +249,48 @@ def test_bwd_long_sequence(ea, dtype, n, H, H_kv):
     err_k = float((dk64.sum(dim=2).abs() / tol_k).max())
     print(f"N={n} {dtype}: identity errors / bounds: dv {err_v:.3f}, dk {err_k:.3f}", flush=True)
     assert err_v <= 1 and err_k <= 1
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_bwd_offsets_past_2_31_elements(ea, oracle_lib, dtype):
+    """Q, K, V, O, dO and the gradients at more than 2^31 elements each
+    (B = 1, H = 32800, N = 1024, d = 64, causal): the gradient kernels
+    address every slice with 64-bit offsets. Inputs are drawn on the device;
+    the slices on both sides of the 32-bit wrap points (2^31 and 2^32 bytes,
+    2^31 elements) and the first and last get the oracle's o and lse and are
+    checked on every element against the oracle's gradients."""
+    N, d, H = 1024, 64, 32800
+    q, k, v = make_qkv_device(1, H, N, d, dtype, seed=32)
+    dout = make_dout_device(1, H, N, d, dtype, seed=32)
+    scale = ea.default_scale(d)
+    o, lse = ea.fwd(q, k, v, causal=True, scale=scale)
+    picks = set()
+    for lim in (2 ** 31 // q.element_size(), 2 ** 32 // q.element_size(), 2 ** 31):
+        first = -(-lim // (N * d))
+        picks |= {t for t in (first - 1, first) if 0 <= t < H}
+    picks = sorted(picks | {0, H - 1})
+    print(f"{dtype}: slices {picks}", flush=True)
+    subs = {}
+    for h in picks:
+        sub = tuple(t[:, h:h + 1].cpu() for t in (q, k, v, dout))
+        o_s, lse_s = _fwd_stats(oracle_lib, sub[0], sub[1], sub[2], True, scale)
+        o[:, h:h + 1] = o_s.cuda()
+        lse[:, h:h + 1] = lse_s.cuda()
+        subs[h] = sub
+    dq, dk, dv = ea.bwd(q, k, v, o, lse, dout, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    n_acc = N / 16 + 32
+    for h, sub in subs.items():
+        rq, rk, rv, eq, ek, ev, zq, zk, zv = oracle_lib.attn_bwd_ref(*sub, True, scale,
+                                                                     error_scales=True)
+        u_s = _score_term(sub[0], sub[1], scale)
+        fq, fk, fv = _flush_terms(*sub, scale)
+        tag = f"slice {h} (offset {h * N * d} elements)"
+        _check(dq[:, h:h + 1], rq, eq, zq, dtype, n_acc, tag + " dq", u_s, fq)
+        _check(dk[:, h:h + 1], rk, ek, zk, dtype, n_acc, tag + " dk", u_s, fk)
+        _check(dv[:, h:h + 1], rv, ev, zv, dtype, n_acc, tag + " dv", u_s, fv)
+    del q, k, v, dout, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])

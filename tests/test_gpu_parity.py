@@ -21,7 +21,8 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_15_amd.inputs import (WORKLOADS, make_dout, make_qkv, make_structured_qkv,
+from exact_attention_15_amd.inputs import (WORKLOADS, make_dout, make_qkv, make_qkv_device,
+                                           make_structured_qkv,
                                            workload_inputs)
 
 pytestmark = pytest.mark.gpu
@@ -201,6 +202,58 @@ def test_attn_fwd_entry_point_two_query_blocks(ea, oracle_lib):
     o_ref, lse_ref = oracle_lib.attn_fwd_ref_rows(q, k, v, False, scale, rows)
     _check(o.cpu().double().numpy().reshape(-1, d)[rows], lse.cpu().double().numpy().reshape(-1)[rows],
            o_ref, lse_ref, torch.bfloat16, f"attn_fwd two query blocks ({len(rows)} sampled rows)", n)
+
+
+def wrap_slices(n_slices, slice_elems, elem_bytes, group=1):
+    """Query slices whose data (or whose K/V slice's data, with `group` query
+    heads per K/V head) ends just before or starts at an offset where 32-bit
+    arithmetic would wrap: 2^31 bytes, 2^32 bytes, 2^31 elements; and the
+    first and last slice."""
+    picks = {0, n_slices - 1}
+    for lim in (2 ** 31 // elem_bytes, 2 ** 32 // elem_bytes, 2 ** 31):
+        first = -(-lim // slice_elems)   # first slice starting at or past lim
+        for t in (first - 1, first):
+            for h in (t, t * group, t * group + group - 1):
+                if 0 <= h < n_slices:
+                    picks.add(h)
+    return sorted(picks)
+
+
+LARGE = [   # (dtype, d, causal, H, H_kv) at B = 1, N = 1024: Q holds more than 2^31 elements
+    (torch.bfloat16, 64, True, 32800, 32800),    # one query block per wave
+    (torch.bfloat16, 64, False, 32800, 32800),   # two query blocks per wave
+    (torch.float16, 128, False, 16400, 8200),    # d = 128, two query heads per K/V head
+    (torch.float32, 64, True, 32800, 32800),
+]
+
+
+@pytest.mark.parametrize("dtype,d,causal,H,H_kv", LARGE,
+                         ids=["bf16-d64-causal", "bf16-d64", "f16-d128-gqa2", "f32-d64-causal"])
+def test_offsets_past_2_31_elements(ea, oracle_lib, dtype, d, causal, H, H_kv):
+    """Q, K, V, O of more than 2^31 elements (4.3-8.6 GB each): every slice
+    is addressed with 64-bit offsets. Inputs are drawn on the device; the
+    slices on both sides of every 32-bit wrap point (bytes and elements, of
+    Q/O and of K/V) and the first and last are checked on every element
+    against the oracle."""
+    N = 1024
+    assert H * N * d > 2 ** 31
+    G = H // H_kv
+    q, k, v = make_qkv_device(1, H, N, d, dtype, seed=31, H_kv=H_kv)
+    scale = ea.default_scale(d)
+    o, lse = ea.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    picks = sorted(set(wrap_slices(H, N * d, q.element_size())) |
+                   set(wrap_slices(H, N * d, q.element_size(), G)))
+    print(f"{dtype} d={d} causal={causal} H={H} H_kv={H_kv}: slices {picks}", flush=True)
+    for h in picks:
+        kh = h // G
+        qs, ks, vs = (t[:, a:a + 1].cpu() for t, a in ((q, h), (k, kh), (v, kh)))
+        o_ref, lse_ref = oracle_lib.attn_fwd_ref(qs, ks, vs, causal, scale)
+        _check(o[:, h:h + 1].cpu().to(torch.float64).numpy(),
+               lse[:, h:h + 1].cpu().to(torch.float64).numpy(), o_ref, lse_ref, dtype,
+               f"slice {h} (Q offset {h * N * d} elements)", N)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
