@@ -3,7 +3,8 @@ bits; and the structured score shapes the running-maximum tests rely on."""
 import numpy as np
 import torch
 
-from exact_attention_15_amd.inputs import WORKLOADS, make_qkv, make_structured_qkv
+from exact_attention_15_amd.inputs import (WORKLOADS, make_dout_device, make_qkv, make_qkv_device,
+                                           make_structured_qkv)
 
 
 def test_seeded_inputs_repeat_bit_for_bit():
@@ -39,3 +40,19 @@ def test_structured_rows_have_the_intended_shape():
     spikes = _tile_maxima(*make_structured_qkv("spikes", 1, 1, n, d, torch.float32, 7)[:2], 5)
     assert np.all(np.diff(spikes[:4]) > 128 * np.log(2)), spikes
     assert abs(spikes[3] - 300.0) < 30.0 and spikes[4] < 10.0, spikes
+
+
+def test_device_draws_repeat_and_follow_the_recipe():
+    """The device-side draws (run here on the CPU generator): same seed, same
+    bits; Q, K, V and dO of the requested shapes and dtype, K and V with
+    H_kv heads; unit variance before rounding."""
+    a = make_qkv_device(1, 4, 256, 64, torch.bfloat16, seed=5, H_kv=2, device="cpu")
+    b = make_qkv_device(1, 4, 256, 64, torch.bfloat16, seed=5, H_kv=2, device="cpu")
+    assert [t.shape for t in a] == [(1, 4, 256, 64), (1, 2, 256, 64), (1, 2, 256, 64)]
+    assert all(t.dtype == torch.bfloat16 for t in a)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    assert not torch.equal(a[1], a[2])
+    x = torch.cat([t.float().flatten() for t in a])
+    assert abs(float(x.mean())) < 0.02 and abs(float(x.std()) - 1.0) < 0.02
+    g = make_dout_device(1, 4, 256, 64, torch.float32, seed=5, device="cpu")
+    assert g.shape == (1, 4, 256, 64) and not torch.equal(g, a[0].float())
