@@ -128,14 +128,22 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, GROUPS == 3 ? 3 : 2) void bwd
     // loop the Q and dO space holds group 1's partial sums.
     static_assert(GROUPS == 1 || 4 * GROUPS * T::kBytes >= 2 * NDB * 16 * kBwdThreads * 4,
                   "reduction space");
-    __shared__ __attribute__((aligned(1024))) char q_lds0[GROUPS * T::kBytes];
-    __shared__ __attribute__((aligned(1024))) char q_lds1[GROUPS * T::kBytes];
-    __shared__ __attribute__((aligned(1024))) char o_lds0[GROUPS * T::kBytes];   // dO
-    __shared__ __attribute__((aligned(1024))) char o_lds1[GROUPS * T::kBytes];
-    __shared__ __attribute__((aligned(16))) float l_lds0[GROUPS * kQStage];      // lse * log2(e)
-    __shared__ __attribute__((aligned(16))) float l_lds1[GROUPS * kQStage];
-    __shared__ __attribute__((aligned(16))) float d_lds0[GROUPS * kQStage];      // -D
-    __shared__ __attribute__((aligned(16))) float d_lds1[GROUPS * kQStage];
+    // One LDS block, the four row-statistic arrays first: their addresses
+    // then fit the 16-bit offset field of an LDS instruction, so one lane
+    // address serves all four (at d = 128 the tiles take 64 KB, and placed
+    // after them the arrays cost three more address registers, spilled).
+    constexpr int kStat = GROUPS * kQStage * 4;       // bytes of one array
+    static_assert((4 * kStat) % 1024 == 0, "tiles stay 1024-byte aligned");
+    __shared__ __attribute__((aligned(1024))) char smem[4 * kStat + 4 * GROUPS * T::kBytes];
+    LDS_AS char* const lds = (LDS_AS char*)smem;
+    LDS_AS float* const l_lds0 = (LDS_AS float*)(lds);                 // lse * log2(e)
+    LDS_AS float* const l_lds1 = (LDS_AS float*)(lds + kStat);
+    LDS_AS float* const d_lds0 = (LDS_AS float*)(lds + 2 * kStat);     // -D
+    LDS_AS float* const d_lds1 = (LDS_AS float*)(lds + 3 * kStat);
+    LDS_AS char* const q_lds0 = lds + 4 * kStat;
+    LDS_AS char* const q_lds1 = q_lds0 + GROUPS * T::kBytes;
+    LDS_AS char* const o_lds0 = q_lds1 + GROUPS * T::kBytes;          // dO
+    LDS_AS char* const o_lds1 = o_lds0 + GROUPS * T::kBytes;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -145,14 +153,10 @@ __global__ __launch_bounds__(kBwdThreads * GROUPS, GROUPS == 3 ? 3 : 2) void bwd
     const int l32 = lane & 31;
     const int g = lane >> 5;
     const int N = (int)p.N;
-    LDS_AS char* const qL[2] = {(LDS_AS char*)q_lds0 + grp * T::kBytes,
-                                (LDS_AS char*)q_lds1 + grp * T::kBytes};
-    LDS_AS char* const oL[2] = {(LDS_AS char*)o_lds0 + grp * T::kBytes,
-                                (LDS_AS char*)o_lds1 + grp * T::kBytes};
-    LDS_AS float* const lL[2] = {(LDS_AS float*)l_lds0 + grp * kQStage,
-                                 (LDS_AS float*)l_lds1 + grp * kQStage};
-    LDS_AS float* const dL[2] = {(LDS_AS float*)d_lds0 + grp * kQStage,
-                                 (LDS_AS float*)d_lds1 + grp * kQStage};
+    LDS_AS char* const qL[2] = {q_lds0 + grp * T::kBytes, q_lds1 + grp * T::kBytes};
+    LDS_AS char* const oL[2] = {o_lds0 + grp * T::kBytes, o_lds1 + grp * T::kBytes};
+    LDS_AS float* const lL[2] = {l_lds0 + grp * kQStage, l_lds1 + grp * kQStage};
+    LDS_AS float* const dL[2] = {d_lds0 + grp * kQStage, d_lds1 + grp * kQStage};
 
     // Item w: key tile kt of K/V slice kv_bh, its steps s0 .. s0 + n_steps - 1.
     const int w = blockIdx.x;
