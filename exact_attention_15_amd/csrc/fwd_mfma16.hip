@@ -58,18 +58,33 @@
 //     registers the S products are about to fill stage the V^T operands
 //     read ahead, and the P registers then stage the K operands.
 //   * Lazy rescale: the exponent base m only moves when a tile's row max
-//     exceeds it by more than 2^8 in probability; otherwise P <= 256 is used
-//     as is. The final O / l does not depend on the base, and a bf16/fp16 P
-//     keeps its relative precision at that magnitude.
+//     exceeds it by more than the threshold T in probability (T = 2^8 for
+//     fp16, whose P must stay far below 65504; 2^64 for bf16, whose P has
+//     fp32's exponent range); otherwise P <= T is used as is. The final
+//     O / l does not depend on the base, and a 16-bit P keeps its relative
+//     precision at any magnitude its type represents.
 //   * The softmax step does not take the row maximum first: it
 //     exponentiates against the current base, then tests whether any packed
-//     P exceeds 2^8 (or overflowed) with 3-input packed 16-bit maxima, eight
+//     P exceeds T (or overflowed) with 3-input packed 16-bit maxima, eight
 //     per tile and query block instead of ~25 instructions for the fp32
 //     maximum, its lane exchange and the comparison. Only if some row fails
 //     does the wave take the maximum and redo the tile against the moved
 //     base; the P it keeps is the same either way. At d = 64 the vector ALU
 //     is the busier unit, so this is +4-5 % at the causal workloads and
 //     +5 % with two query blocks; at d = 128 it is +0-1 %.
+//   * bf16 at d = 64 goes one step further: a first pass takes no overflow
+//     test at all (each row keeps the base tile 0 gave it), and the test
+//     moves to the end of the work item, on the row sums: every P of a row
+//     is at most its l, so a row with l <= T never had a P above T, and its
+//     bits are those the per-tile test would give. If some row fails (its
+//     score maximum rose by more than ~64 log2 units after tile 0, or a P
+//     overflowed), the workgroup computes the item again with the per-tile
+//     test, in a function of its own so that the rare path takes nothing
+//     from the main path's registers. Which rows share a workgroup thus
+//     never changes a row's bits. On gfx950 a full-rate vector instruction
+//     (the maxima, the compare) hardly overlaps another wave's MFMAs, while
+//     exp2 and the bf16 packs do: +3 % at the causal headline, +4 % with two
+//     query blocks.
 //   * The softmax row sum l runs on the matrix core as well: a 16x16x32
 //     MFMA with a constant 0/1 A operand sums the P operand of the P.V step
 //     over its keys (four per tile and query block), which takes ~60 fp32
@@ -95,7 +110,12 @@ namespace attn {
 namespace {
 
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kRescaleThreshold = 8.0f;   // log2 units: P may reach 2^8
+// Largest P the lazy rescale lets through (log2 units): 2^8 for fp16, whose
+// P must stay far below its 65504 maximum; 2^64 for bf16, whose P has fp32's
+// exponent range and the same relative precision at any magnitude (O then
+// stays finite for |V| up to ~2^60).
+template <bool IS_BF16>
+constexpr float rescale_threshold() { return IS_BF16 ? 64.0f : 8.0f; }
 constexpr int kBlockN = 64;                 // keys per K/V tile
 constexpr int kThreads = 512;               // 8 waves
 constexpr int kWaves = kThreads / 64;
@@ -201,10 +221,12 @@ __device__ __forceinline__ float permlane16_swap_y(float x, float y) {
     return __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-// d = 64 with one query block: four waves per SIMD (two workgroups per
-// compute unit), i.e. at most 128 VGPRs; the others take two waves per SIMD.
-template <bool IS_BF16, int D, bool CAUSAL, int QB>
-__global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_kernel(FwdParams p) {
+// One pass of a workgroup over its work item. OPT (bf16 only): no overflow
+// test per tile; returns false, without writing anything, when some row of
+// the item needs the exact pass (decided by the whole workgroup).
+template <bool IS_BF16, int D, bool CAUSAL, int QB, bool OPT>
+__device__ __forceinline__ bool fwd16_pass(const FwdParams& p, int tid, int bid) {
+    static_assert(!OPT || (IS_BF16 && D == 64), "the pass without the overflow test is bf16, d = 64 only");
     static_assert(QB == 1 || (QB == 2 && D == 64), "two query blocks per wave only at d = 64");
     using Op = Op16<IS_BF16>;
     using T = Tile<D>;
@@ -218,7 +240,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
     __shared__ __attribute__((aligned(1024))) char v_lds0[T::kBytes];
     __shared__ __attribute__((aligned(1024))) char v_lds1[T::kBytes];
 
-    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2;              // 0: leads, 1: one step behind
     const int lane = tid & 63;
@@ -226,7 +247,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
     const int g = lane >> 5;
 
     // Work item, longest query tiles first (fwd_order.h).
-    const fwdorder::Item it = fwdorder::item(p.xcd_order != 0, (int)blockIdx.x, p.n_qtiles, p.BH,
+    const fwdorder::Item it = fwdorder::item(p.xcd_order != 0, bid, p.n_qtiles, p.BH,
                                              p.BH_kv, p.H_kv, p.G);
     const int tile = it.tile;
     const SliceIds ids = {it.bh, it.kv_bh};
@@ -356,11 +377,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
             float mx = max3(mxa, mxb, max3(s[qb][0][15], s[qb][1][15], s[qb][1][15]));
             mx = half_swap_max(mx) * c2;
             m_old[qb] = m_used[qb];
-            need[qb] = mx > m_old[qb] + kRescaleThreshold;
+            need[qb] = mx > m_old[qb] + rescale_threshold<IS_BF16>();
             m_used[qb] = need[qb] ? mx : m_old[qb];
         }
     };
 
+    // Set by any wave whose rows need the exact pass.
+    __shared__ int redo_flag;
+    if (OPT && tid == 0) redo_flag = 0;
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this lane's copy of K(0)
     __syncthreads();
 
@@ -493,10 +517,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
 
     // VALU step of tile jj: online softmax of S(jj) into P for every query
     // block, and the rescale of O where the exponent base moved. In the
-    // common case (no P above 2^8) it is one straight stretch of fma, exp2,
-    // pack and packed maxima; the row maxima and the rescale branches only
-    // run on tile 0 and where a base moves.
-    auto valu_step = [&](int jj) __attribute__((always_inline)) {
+    // common case (no P above the threshold) it is one straight stretch of
+    // fma, exp2, pack and packed maxima (no maxima in a first pass, opt);
+    // the row maxima and the rescale branches only run on tile 0 and where
+    // a base moves.
+    auto valu_step = [&](int jj, bool opt) __attribute__((always_inline)) {
         // (Tiles past this wave's rows go to dead_steps and do not get here;
         // the check is kept for the register allocation it leads to: without
         // it the two-block kernel takes two more VGPRs.)
@@ -510,7 +535,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
             // fp16 keep their order up to ~2^121; beyond that they read as
             // inf or NaN, which the test below also catches (as it catches
             // an overflowed P, inf or NaN).
-            uint32_t c = 0u;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const float m_sub = m_used[qb];
@@ -523,6 +547,24 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
                         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb2 >> 1][i + 1], c2, -m_sub));
                         pk[qb][kb2][e] = Op::pack2(p0, p1);
                     }
+            }
+            if (opt) {
+                // bf16 first pass: no overflow test (l is checked at the end).
+                // The empty asm keeps P inside this step: with nothing here
+                // reading it, the compiler would sink its computation past
+                // the barrier into the next MFMA step, next to the products
+                // that use it.
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    need[qb] = false;
+#pragma unroll
+                    for (int kb2 = 0; kb2 < 4; ++kb2) asm volatile("" : "+v"(pk[qb][kb2]));
+                }
+                return;
+            }
+            uint32_t c = 0u;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
                 uint32_t cq = pk_max3_f16(pk[qb][0][0], pk[qb][0][1], pk[qb][0][2]);
                 cq = pk_max3_f16(cq, pk[qb][0][3], pk[qb][1][0]);
                 cq = pk_max3_f16(cq, pk[qb][1][1], pk[qb][1][2]);
@@ -533,19 +575,20 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
                 cq = pk_max3_f16(cq, pk[qb][3][3], pk[qb][3][3]);
                 c = qb == 0 ? cq : pk_max3_f16(c, cq, cq);
             }
-            // 2^8 as a packed value read as fp16 (bf16 0x4380 reads 3.75).
-            const _Float16 lim = IS_BF16 ? (_Float16)3.75f : (_Float16)256.0f;
+            // The threshold as a packed value read as fp16: bf16 2^64 (0x5f80)
+            // reads 480, fp16 2^8 is 256.
+            const _Float16 lim = IS_BF16 ? (_Float16)480.0f : (_Float16)256.0f;
             const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(c & 0xffffu));
             const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(c >> 16));
             const bool over = !(lo <= lim) || !(hi <= lim);
             if (__builtin_amdgcn_ballot_w64(over) == 0) {
-                // P <= 2^8 everywhere: every base stays.
+                // No P above the threshold: every base stays.
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) need[qb] = false;
                 return;
             }
         }
-        // Tile 0, or some P above 2^8: the exact rule, on S.
+        // Tile 0, or some P above the threshold: the exact rule, on S.
         row_max_need();
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -604,13 +647,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
     };
     // One tile: MFMA step, barrier, VALU step, barrier (group A first waits
     // for its copies, which the next step reads).
-    auto tile_steps = [&](int j, auto par_tag, auto has_pv_tag) __attribute__((always_inline)) {
+    auto tile_steps = [&](int j, auto par_tag, auto has_pv_tag, bool opt) __attribute__((always_inline)) {
         copies(j, par_tag);
         ATTN_PROBE(j);
         mfma_step(j, par_tag, has_pv_tag, std::true_type{});
         ATTN_PROBE(j + 1);
         barrier();
-        valu_step(j);
+        valu_step(j, opt);
         if (grp == 0) __builtin_amdgcn_s_waitcnt(0x0f70);
         ATTN_PROBE(j + 2);
         barrier();
@@ -639,17 +682,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
         barrier();
     };
 
+    constexpr bool opt = OPT;
     // Group B runs one step behind group A.
     if (grp == 1) barrier();
-    tile_steps(0, P0{}, NoPV{});
+    tile_steps(0, P0{}, NoPV{}, opt);
     int j = 1;
     // (Without a mask n_live is n_tiles.)
     const int n_loop = CAUSAL ? n_live : n_tiles;
     for (; j + 1 < n_loop; j += 2) {
-        tile_steps(j, P1{}, WithPV{});
-        tile_steps(j + 1, P0{}, WithPV{});
+        tile_steps(j, P1{}, WithPV{}, opt);
+        tile_steps(j + 1, P0{}, WithPV{}, opt);
     }
-    if (j < n_loop) tile_steps(j, P1{}, WithPV{});
+    if (j < n_loop) tile_steps(j, P1{}, WithPV{}, opt);
     if constexpr (CAUSAL) {
         j = n_live;
         if (j < n_tiles) {
@@ -665,6 +709,25 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
     if (n_tiles & 1) mfma_step(n_tiles, P1{}, WithPV{}, std::false_type{});
     else mfma_step(n_tiles, P0{}, WithPV{}, std::false_type{});
     if (grp == 0) barrier();
+
+    if constexpr (OPT) {
+        // Without the per-tile test every row kept the base tile 0 gave it.
+        // A P above the threshold would make its row's l (at least every P
+        // of the row) exceed it, so a row with l <= 2^64 saw no such P, and
+        // its bits are those of the exact pass, which only moves a base where
+        // some P exceeds 2^64. If any row of the item fails (score maxima
+        // that rise by more than ~64 log2 units after tile 0, or an
+        // overflow), the workgroup hands the item to the exact pass.
+        bool bad = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            bad = bad || !(permlane16_swap_x(lacc[qb][0], lacc[qb][1]) <= 0x1p64f);
+        if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo_flag = 1;
+        __syncthreads();
+        // (Read as a wave-uniform value, so that the branch is uniform too
+        // and nothing of this pass stays live into the exact one.)
+        if (__builtin_amdgcn_readfirstlane(redo_flag) != 0) return false;
+    }
 
     // Epilogue: O = O~ / l, rounded once to the output type; lse in fp32.
 #pragma unroll
@@ -686,6 +749,48 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
                 }
             if (g == 0) p.lse[(size_t)bh * N + qi] = (m_used[qb] + log2f(l_tot)) * kLn2;
         }
+    }
+    return true;
+}
+
+// The exact pass for a bf16 work item whose first pass failed its check: a
+// function of its own, so that its registers are allocated apart from the
+// kernel's main path, which it follows only in that rare case.
+// (Arguments reach a function in vector registers: the parameters and the
+// workgroup index are made wave-uniform again; the thread index is passed
+// in, so that the kernel need not keep the hardware's work-item ids for the
+// call.)
+template <bool IS_BF16, int D, bool CAUSAL, int QB>
+__device__ __attribute__((noinline)) void fwd16_exact_item(FwdParams pv, int tid, int bid) {
+    static_assert(sizeof(FwdParams) % 4 == 0, "FwdParams is read as 32-bit words");
+    uint32_t w[sizeof(FwdParams) / 4];
+    __builtin_memcpy(w, &pv, sizeof(FwdParams));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(FwdParams) / 4); ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+    FwdParams p;
+    __builtin_memcpy(&p, w, sizeof(FwdParams));
+    (void)fwd16_pass<IS_BF16, D, CAUSAL, QB, false>(p, tid, __builtin_amdgcn_readfirstlane(bid));
+}
+
+// d = 64 with one query block: four waves per SIMD (two workgroups per
+// compute unit), i.e. at most 128 VGPRs; the others take two waves per SIMD.
+template <bool IS_BF16, int D, bool CAUSAL, int QB>
+__global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_kernel(FwdParams p) {
+    const int tid = threadIdx.x, bid = blockIdx.x;
+    // bf16 at d = 64: first the pass without the per-tile overflow test
+    // (+3 % at the causal workloads, where the vector ALU sets the pace); at
+    // d = 128 (+0.8 % alone, and the call into the exact pass costs more
+    // than that there) and for fp16 the exact pass only.
+    if constexpr (IS_BF16 && D == 64) {
+        if (!fwd16_pass<IS_BF16, D, CAUSAL, QB, true>(p, tid, bid)) {
+            fwd16_exact_item<IS_BF16, D, CAUSAL, QB>(p, tid, bid);
+            // The wave ends here: no path leads from the call back into the
+            // first pass's epilogue (whose values would then have to live
+            // across the call).
+            __builtin_amdgcn_endpgm();
+        }
+    } else {
+        (void)fwd16_pass<IS_BF16, D, CAUSAL, QB, false>(p, tid, bid);
     }
 }
 

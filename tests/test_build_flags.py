@@ -3,7 +3,9 @@ library's own flags (hipcc cross-compiles without a GPU):
 * no packed fp32 VALU form (v_pk_fma_f32, v_pk_mul_f32, v_pk_add_f32):
   hipcc emits them from ordinary float code unless the packed-fp32-ops
   target feature is turned off, as the build does;
-* no register spills (scratch memory per lane) in any kernel."""
+* no register spills (scratch memory per lane) in any kernel, except the
+  stack frame of the bf16 d = 64 forward's call into its exact pass, whose
+  scratch instructions must all sit in the one block that makes the call."""
 import os
 import re
 import subprocess
@@ -65,15 +67,47 @@ def test_no_packed_fp32_instruction_in_any_kernel(compiled):
     assert not any(found.values()), found
 
 
+# The bf16 d = 64 forward kernels call their exact pass (a function of its
+# own) in the rare case: the call's frame is scratch, but nothing outside
+# the calling block may touch it.
+CALLS_EXACT_PASS = re.compile(r"fwd16_kernelILb1ELi64E")
+
+
+def _function_asm(asm, name):
+    start = asm.index(f"\n{name}:")
+    return asm[start:asm.index(".Lfunc_end", start)]
+
+
+def _blocks(fn_asm):
+    """Basic blocks of one function's assembly, split at labels."""
+    return re.split(r"\n(?=\.LBB\d+_\d+:)", fn_asm)
+
+
 def test_no_register_spills(compiled):
     kernels = {k: v for _, (_, sc) in compiled.items() for k, v in sc.items()}
     assert len(kernels) >= 30, sorted(kernels)   # every instantiation was seen
     over = {}
     for k, v in kernels.items():
         allowed = next((a for frag, a in SCRATCH_ALLOWED.items() if frag in k), 0)
-        if v > allowed:
+        if v > allowed and not CALLS_EXACT_PASS.search(k):
             over[k] = v
     assert not over, over
+
+
+def test_scratch_only_around_the_exact_pass_call(compiled):
+    """In the kernels that call the exact pass, every scratch access is in
+    the block that makes the call (saves and reloads around it): the main
+    path, the tile loop included, spills nothing."""
+    asm = compiled["fwd_mfma16.hip"][0]
+    names = [k for k in compiled["fwd_mfma16.hip"][1] if CALLS_EXACT_PASS.search(k)]
+    assert len(names) == 3, names
+    for name in names:
+        blocks = _blocks(_function_asm(asm, name))
+        calls = [b for b in blocks if "s_swappc_b64" in b]
+        assert len(calls) == 1, name
+        stray = [b.split("\n", 1)[0] for b in blocks
+                 if re.search(r"\bscratch_(load|store)", b) and "s_swappc_b64" not in b]
+        assert not stray, (name, stray)
 
 
 def _waves_per_simd(regs):
