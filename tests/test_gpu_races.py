@@ -89,6 +89,34 @@ def test_forward_two_query_blocks_matches_probe_build(libs, dtype):
           f"forward two query blocks {dtype}")
 
 
+@pytest.mark.parametrize("causal,H", [(False, 4), (True, 4), (False, 64)],
+                         ids=["full", "causal", "full-two-query-blocks"])
+def test_forward_exact_pass_matches_probe_build(libs, causal, H):
+    """bf16 d = 64 work items that the first pass hands to the exact pass:
+    in every second slice, query rows 900-911 and 1400-1411 meet one key
+    (index 500, visible to them under the causal mask too) with a score
+    ~+100 nats, past fp32's exp2 range against their base; the other slices
+    stay in the first pass. Both builds must agree bit for bit, the exact pass included (its
+    own LDS buffers, its own copies and barriers). H = 64 runs the
+    two-query-block kernel."""
+    ea, lib, probe = libs
+    n, d = 1777, 64
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7380 + H)
+    q = torch.randn((1, H, n, d), generator=g)
+    k = torch.randn((1, H, n, d), generator=g)
+    v = torch.randn((1, H, n, d), generator=g)
+    u = torch.randint(0, 2, (d,), generator=g).to(torch.float32) * 2.0 - 1.0
+    q[:, ::2, 900:912] = 3.0 * u
+    q[:, ::2, 1400:1412] = 3.0 * u
+    k[:, ::2, 500] = 4.0 * u
+    q, k, v = (t.to(torch.bfloat16).cuda() for t in (q, k, v))
+    a = _fwd(ea, lib, q, k, v, causal)
+    b = _fwd(ea, probe, q, k, v, causal)
+    _same(a, b, f"forward exact pass causal={causal} H={H}")
+    assert torch.isfinite(a[0]).all() and float(a[1][0, 0, 900:912].min()) > 90.0
+
+
 @pytest.mark.parametrize("dtype,d,H,H_kv", [
     (torch.bfloat16, 64, 4, 2),    # three wave groups per dK/dV item
     (torch.bfloat16, 64, 4, 4),
