@@ -58,9 +58,9 @@
 //     registers the S products are about to fill stage the V^T operands
 //     read ahead, and the P registers then stage the K operands.
 //   * Lazy rescale: the exponent base m only moves when a tile's row max
-//     exceeds it by more than the threshold T in probability (T = 2^8 for
-//     fp16, whose P must stay far below 65504; 2^64 for bf16, whose P has
-//     fp32's exponent range); otherwise P <= T is used as is. The final
+//     exceeds it by more than the threshold T in probability (T = 2^15 for
+//     fp16, below its 65504 maximum; 2^64 for bf16, whose P has fp32's
+//     exponent range); otherwise P <= T is used as is. The final
 //     O / l does not depend on the base, and a 16-bit P keeps its relative
 //     precision at any magnitude its type represents.
 //   * The softmax step does not take the row maximum first: it
@@ -72,19 +72,20 @@
 //     base; the P it keeps is the same either way. At d = 64 the vector ALU
 //     is the busier unit, so this is +4-5 % at the causal workloads and
 //     +5 % with two query blocks; at d = 128 it is +0-1 %.
-//   * bf16 at d = 64 goes one step further: a first pass takes no overflow
-//     test at all (each row keeps the base tile 0 gave it), and the test
-//     moves to the end of the work item, on the row sums: every P of a row
-//     is at most its l, so a row with l <= T never had a P above T, and its
-//     bits are those the per-tile test would give. If some row fails (its
-//     score maximum rose by more than ~64 log2 units after tile 0, or a P
-//     overflowed), the workgroup computes the item again with the per-tile
-//     test, in a function of its own so that the rare path takes nothing
-//     from the main path's registers. Which rows share a workgroup thus
+//   * At d = 64 the kernel goes one step further: a first pass takes no
+//     overflow test at all (each row keeps the base tile 0 gave it), and
+//     the test moves to the end of the work item, on the row sums: every P
+//     of a row is at most its l, so a row with l <= T never had a P above
+//     T, and its bits are those the per-tile test would give. If some row
+//     fails (its score maximum rose by more than ~64 (bf16) or ~15 (fp16)
+//     log2 units after tile 0, or many keys came close to T), the
+//     workgroup computes the item again with the per-tile test, in a
+//     function of its own so that the rare path takes nothing from the main
+//     path's registers. Which rows share a workgroup thus
 //     never changes a row's bits. On gfx950 a full-rate vector instruction
 //     (the maxima, the compare) hardly overlaps another wave's MFMAs, while
-//     exp2 and the bf16 packs do: +3 % at the causal headline, +4 % with two
-//     query blocks.
+//     exp2 and the 16-bit packs do: +3 % at the causal workloads, +4 % with
+//     two query blocks.
 //   * The softmax row sum l runs on the matrix core as well: a 16x16x32
 //     MFMA with a constant 0/1 A operand sums the P operand of the P.V step
 //     over its keys (four per tile and query block), which takes ~60 fp32
@@ -110,12 +111,12 @@ namespace attn {
 namespace {
 
 constexpr float kLn2 = 0.693147180559945309f;
-// Largest P the lazy rescale lets through (log2 units): 2^8 for fp16, whose
-// P must stay far below its 65504 maximum; 2^64 for bf16, whose P has fp32's
-// exponent range and the same relative precision at any magnitude (O then
-// stays finite for |V| up to ~2^60).
+// Largest P the lazy rescale lets through (log2 units): 2^15 for fp16, below
+// its 65504 maximum; 2^64 for bf16, whose P has fp32's exponent range and the
+// same relative precision at any magnitude (O then stays finite for |V| up
+// to ~2^60). Both keep O and l, which accumulate in fp32, far from overflow.
 template <bool IS_BF16>
-constexpr float rescale_threshold() { return IS_BF16 ? 64.0f : 8.0f; }
+constexpr float rescale_threshold() { return IS_BF16 ? 64.0f : 15.0f; }
 constexpr int kBlockN = 64;                 // keys per K/V tile
 constexpr int kThreads = 512;               // 8 waves
 constexpr int kWaves = kThreads / 64;
@@ -221,12 +222,12 @@ __device__ __forceinline__ float permlane16_swap_y(float x, float y) {
     return __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-// One pass of a workgroup over its work item. OPT (bf16 only): no overflow
+// One pass of a workgroup over its work item. OPT (d = 64 only): no overflow
 // test per tile; returns false, without writing anything, when some row of
 // the item needs the exact pass (decided by the whole workgroup).
 template <bool IS_BF16, int D, bool CAUSAL, int QB, bool OPT>
 __device__ __forceinline__ bool fwd16_pass(const FwdParams& p, int tid, int bid) {
-    static_assert(!OPT || (IS_BF16 && D == 64), "the pass without the overflow test is bf16, d = 64 only");
+    static_assert(!OPT || D == 64, "the pass without the overflow test is d = 64 only");
     static_assert(QB == 1 || (QB == 2 && D == 64), "two query blocks per wave only at d = 64");
     using Op = Op16<IS_BF16>;
     using T = Tile<D>;
@@ -549,7 +550,7 @@ __device__ __forceinline__ bool fwd16_pass(const FwdParams& p, int tid, int bid)
                     }
             }
             if (opt) {
-                // bf16 first pass: no overflow test (l is checked at the end).
+                // First pass: no overflow test (l is checked at the end).
                 // The empty asm keeps P inside this step: with nothing here
                 // reading it, the compiler would sink its computation past
                 // the barrier into the next MFMA step, next to the products
@@ -576,8 +577,8 @@ __device__ __forceinline__ bool fwd16_pass(const FwdParams& p, int tid, int bid)
                 c = qb == 0 ? cq : pk_max3_f16(c, cq, cq);
             }
             // The threshold as a packed value read as fp16: bf16 2^64 (0x5f80)
-            // reads 480, fp16 2^8 is 256.
-            const _Float16 lim = IS_BF16 ? (_Float16)480.0f : (_Float16)256.0f;
+            // reads 480, fp16 2^15 is 32768.
+            const _Float16 lim = IS_BF16 ? (_Float16)480.0f : (_Float16)32768.0f;
             const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(c & 0xffffu));
             const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(c >> 16));
             const bool over = !(lo <= lim) || !(hi <= lim);
@@ -712,16 +713,17 @@ __device__ __forceinline__ bool fwd16_pass(const FwdParams& p, int tid, int bid)
 
     if constexpr (OPT) {
         // Without the per-tile test every row kept the base tile 0 gave it.
-        // A P above the threshold would make its row's l (at least every P
-        // of the row) exceed it, so a row with l <= 2^64 saw no such P, and
-        // its bits are those of the exact pass, which only moves a base where
-        // some P exceeds 2^64. If any row of the item fails (score maxima
-        // that rise by more than ~64 log2 units after tile 0, or an
-        // overflow), the workgroup hands the item to the exact pass.
+        // A P above the threshold T would make its row's l (at least every P
+        // of the row) exceed it, so a row with l <= T saw no such P, and its
+        // bits are those of the exact pass, which only moves a base where
+        // some P exceeds T. If any row of the item fails (score maxima that
+        // rise by more than log2 T after tile 0, an overflow, or, for fp16,
+        // many keys close to T), the workgroup hands the item to the exact
+        // pass.
         bool bad = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-            bad = bad || !(permlane16_swap_x(lacc[qb][0], lacc[qb][1]) <= 0x1p64f);
+            bad = bad || !(permlane16_swap_x(lacc[qb][0], lacc[qb][1]) <= (IS_BF16 ? 0x1p64f : 0x1p15f));
         if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) redo_flag = 1;
         __syncthreads();
         // (Read as a wave-uniform value, so that the branch is uniform too
@@ -777,11 +779,11 @@ __device__ __attribute__((noinline)) void fwd16_exact_item(FwdParams pv, int tid
 template <bool IS_BF16, int D, bool CAUSAL, int QB>
 __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_kernel(FwdParams p) {
     const int tid = threadIdx.x, bid = blockIdx.x;
-    // bf16 at d = 64: first the pass without the per-tile overflow test
-    // (+3 % at the causal workloads, where the vector ALU sets the pace); at
-    // d = 128 (+0.8 % alone, and the call into the exact pass costs more
-    // than that there) and for fp16 the exact pass only.
-    if constexpr (IS_BF16 && D == 64) {
+    // d = 64: first the pass without the per-tile overflow test (+3 % at
+    // the causal workloads, +4 % with two query blocks); at d = 128 (+0.8 %
+    // alone, and the call into the exact pass costs more than that there)
+    // the exact pass only.
+    if constexpr (D == 64) {
         if (!fwd16_pass<IS_BF16, D, CAUSAL, QB, true>(p, tid, bid)) {
             fwd16_exact_item<IS_BF16, D, CAUSAL, QB>(p, tid, bid);
             // The wave ends here: no path leads from the call back into the

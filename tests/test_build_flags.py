@@ -4,7 +4,7 @@ library's own flags (hipcc cross-compiles without a GPU):
   hipcc emits them from ordinary float code unless the packed-fp32-ops
   target feature is turned off, as the build does;
 * no register spills (scratch memory per lane) in any kernel, except the
-  stack frame of the bf16 d = 64 forward's call into its exact pass, whose
+  stack frame of the d = 64 16-bit forward's call into its exact pass, whose
   scratch instructions must all sit in the one block that makes the call."""
 import os
 import re
@@ -67,10 +67,10 @@ def test_no_packed_fp32_instruction_in_any_kernel(compiled):
     assert not any(found.values()), found
 
 
-# The bf16 d = 64 forward kernels call their exact pass (a function of its
-# own) in the rare case: the call's frame is scratch, but nothing outside
-# the calling block may touch it.
-CALLS_EXACT_PASS = re.compile(r"fwd16_kernelILb1ELi64E")
+# The d = 64 16-bit forward kernels call their exact pass (a function of
+# its own) in the rare case: the call's frame is scratch, but nothing
+# outside the calling block may touch it.
+CALLS_EXACT_PASS = re.compile(r"fwd16_kernelILb[01]ELi64E")
 
 
 def _function_asm(asm, name):
@@ -100,7 +100,7 @@ def test_scratch_only_around_the_exact_pass_call(compiled):
     path, the tile loop included, spills nothing."""
     asm = compiled["fwd_mfma16.hip"][0]
     names = [k for k in compiled["fwd_mfma16.hip"][1] if CALLS_EXACT_PASS.search(k)]
-    assert len(names) == 3, names
+    assert len(names) == 6, names
     for name in names:
         blocks = _blocks(_function_asm(asm, name))
         calls = [b for b in blocks if "s_swappc_b64" in b]

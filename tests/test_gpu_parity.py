@@ -344,19 +344,21 @@ def test_forced_variants_are_bit_identical(ea, dtype):
         ea.debug_set_fwd_variant()
 
 
-def test_bf16_exact_pass_keeps_bits_across_variants(ea, oracle_lib):
-    """bf16 at d = 64 runs a first pass without the per-tile overflow test
-    and hands a work item to the exact pass when some row's l exceeds 2^64.
-    Here one key (index 700) has a score of ~+100 nats for the query rows
-    300-310 only (their maximum jumps past fp32's exp2 range, so their
-    items take the exact pass) and of up to ~+15 nats for the others (P up
-    to ~2^22 against their base, kept by the first pass). With one query
-    block per wave (256-row items) rows 0-255 stay in the first pass; with
-    two (512-row items) they share an item with the spiking rows and are
-    computed by the exact pass: both must give the same bits, and every row
-    must match the oracle."""
+@pytest.mark.parametrize("dtype,spike", [(torch.bfloat16, 4.0), (torch.float16, 1.0)],
+                         ids=["bf16", "f16"])
+def test_exact_pass_keeps_bits_across_variants(ea, oracle_lib, dtype, spike):
+    """At d = 64 a first pass runs without the per-tile overflow test and
+    hands a work item to the exact pass when some row's l exceeds the
+    threshold T (2^64 bf16, 2^15 fp16). Here one key (index 700) has a
+    score of 192 spike / 8 nats (~96 bf16, ~24 fp16) for the query rows
+    300-310 only, far past T against their base, so their items take the
+    exact pass, and of spike / 8 (u . q) for the others (u . q ~ N(0, 64):
+    P up to ~2^22 against their base for bf16, ~2^6 for fp16, within T).
+    With one query block per wave (256-row items) rows 0-255 stay in the
+    first pass; with two (512-row items) they share an item with the
+    spiking rows and are computed by the exact pass: both must give the
+    same bits, and every row must match the oracle."""
     B, H, n, d = 1, 2, 1024, 64
-    dtype = torch.bfloat16
     g = torch.Generator(device="cpu")
     g.manual_seed(9100)
     q = torch.randn((B, H, n, d), generator=g)
@@ -364,7 +366,7 @@ def test_bf16_exact_pass_keeps_bits_across_variants(ea, oracle_lib):
     v = torch.randn((B, H, n, d), generator=g)
     u = torch.randint(0, 2, (d,), generator=g).to(torch.float32) * 2.0 - 1.0
     q[:, :, 300:311] = 3.0 * u + 0.25 * torch.randn((B, H, 11, d), generator=g)
-    k[:, :, 700] = 4.0 * u
+    k[:, :, 700] = spike * u
     q, k, v = (t.to(dtype) for t in (q, k, v))
     scale = ea.default_scale(d)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
@@ -378,12 +380,12 @@ def test_bf16_exact_pass_keeps_bits_across_variants(ea, oracle_lib):
         ea.debug_set_fwd_variant()
     (o1, l1), (o2, l2) = outs
     same = torch.equal(o1, o2) and torch.equal(l1, l2)
-    print(f"one vs two query blocks around the exact pass: identical={same}", flush=True)
+    print(f"{dtype}: one vs two query blocks around the exact pass: identical={same}", flush=True)
     assert same
     o_ref, lse_ref = oracle_lib.attn_fwd_ref(q, k, v, False, scale)
     _check(o1.cpu().to(torch.float64).numpy(), l1.cpu().to(torch.float64).numpy(), o_ref, lse_ref,
-           dtype, "bf16 d=64 spiking rows 300-310", n)
-    assert float(lse_ref[0, :, 300:311].min()) > 90.0   # the spiking rows
+           dtype, f"{dtype} d=64 spiking rows 300-310", n)
+    assert float(lse_ref[0, :, 300:311].min()) > 20.0 * spike   # the spiking rows
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16],

@@ -89,10 +89,11 @@ def test_forward_two_query_blocks_matches_probe_build(libs, dtype):
           f"forward two query blocks {dtype}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("causal,H", [(False, 4), (True, 4), (False, 64)],
                          ids=["full", "causal", "full-two-query-blocks"])
-def test_forward_exact_pass_matches_probe_build(libs, causal, H):
-    """bf16 d = 64 work items that the first pass hands to the exact pass:
+def test_forward_exact_pass_matches_probe_build(libs, causal, H, dtype):
+    """d = 64 work items that the first pass hands to the exact pass:
     in every second slice, query rows 900-911 and 1400-1411 meet one key
     (index 500, visible to them under the causal mask too) with a score
     ~+100 nats, past fp32's exp2 range against their base; the other slices
@@ -110,10 +111,10 @@ def test_forward_exact_pass_matches_probe_build(libs, causal, H):
     q[:, ::2, 900:912] = 3.0 * u
     q[:, ::2, 1400:1412] = 3.0 * u
     k[:, ::2, 500] = 4.0 * u
-    q, k, v = (t.to(torch.bfloat16).cuda() for t in (q, k, v))
+    q, k, v = (t.to(dtype).cuda() for t in (q, k, v))
     a = _fwd(ea, lib, q, k, v, causal)
     b = _fwd(ea, probe, q, k, v, causal)
-    _same(a, b, f"forward exact pass causal={causal} H={H}")
+    _same(a, b, f"forward exact pass {dtype} causal={causal} H={H}")
     assert torch.isfinite(a[0]).all() and float(a[1][0, 0, 900:912].min()) > 90.0
 
 
