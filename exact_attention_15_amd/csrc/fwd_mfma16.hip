@@ -776,14 +776,12 @@ __device__ __attribute__((noinline)) void fwd16_exact_item(FwdParams pv, int tid
 
 // d = 64 with one query block: four waves per SIMD (two workgroups per
 // compute unit), i.e. at most 128 VGPRs; the others take two waves per SIMD.
-template <bool IS_BF16, int D, bool CAUSAL, int QB>
+// FIRST: the pass without the per-tile overflow test first (d = 64 only).
+template <bool IS_BF16, int D, bool CAUSAL, int QB, bool FIRST>
 __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_kernel(FwdParams p) {
+    static_assert(!FIRST || D == 64, "the first pass is d = 64 only");
     const int tid = threadIdx.x, bid = blockIdx.x;
-    // d = 64: first the pass without the per-tile overflow test (+3 % at
-    // the causal workloads, +4 % with two query blocks); at d = 128 (+0.8 %
-    // alone, and the call into the exact pass costs more than that there)
-    // the exact pass only.
-    if constexpr (D == 64) {
+    if constexpr (FIRST) {
         if (!fwd16_pass<IS_BF16, D, CAUSAL, QB, true>(p, tid, bid)) {
             fwd16_exact_item<IS_BF16, D, CAUSAL, QB>(p, tid, bid);
             // The wave ends here: no path leads from the call back into the
@@ -795,6 +793,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
         (void)fwd16_pass<IS_BF16, D, CAUSAL, QB, false>(p, tid, bid);
     }
 }
+
+// Sequence length up to which fp16 takes the first pass: its check, l <= 2^15,
+// holds on typical rows of up to ~32k keys (l ~ 5600 at N = 16384 on
+// i.i.d. inputs), but rows of many more keys with flat scores would fail it
+// and pay for both passes. bf16 (2^64) always takes it.
+constexpr int64_t kFp16FirstPassMaxN = 16384;
 
 template <bool IS_BF16, int D, bool CAUSAL, int QB>
 hipError_t launch_qb(FwdParams p, hipStream_t s) {
@@ -809,7 +813,18 @@ hipError_t launch_qb(FwdParams p, hipStream_t s) {
     if (p.force_order == 1) p.xcd_order = 0;
     if (p.force_order == 2 && fwdorder::xcd_major_applies(p.BH_kv)) p.xcd_order = 1;
     const dim3 grid((unsigned)(p.n_qtiles * p.BH));
-    hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL, QB>), grid, dim3(kThreads), 0, s, p);
+    // d = 64: first the pass without the per-tile overflow test (+3 % at
+    // the causal workloads, +4 % with two query blocks); at d = 128 (+0.8 %
+    // alone, and the call into the exact pass costs more than that there)
+    // the exact pass only.
+    if constexpr (D == 64) {
+        if (IS_BF16 || p.N <= kFp16FirstPassMaxN) {
+            hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL, QB, true>), grid, dim3(kThreads), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (!(D == 64 && IS_BF16))
+        hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL, QB, false>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

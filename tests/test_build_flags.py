@@ -67,10 +67,11 @@ def test_no_packed_fp32_instruction_in_any_kernel(compiled):
     assert not any(found.values()), found
 
 
-# The d = 64 16-bit forward kernels call their exact pass (a function of
-# its own) in the rare case: the call's frame is scratch, but nothing
-# outside the calling block may touch it.
-CALLS_EXACT_PASS = re.compile(r"fwd16_kernelILb[01]ELi64E")
+# The d = 64 16-bit forward kernels with the first pass (last template
+# argument true) call their exact pass (a function of its own) in the rare
+# case: the call's frame is scratch, but nothing outside the calling block
+# may touch it.
+CALLS_EXACT_PASS = re.compile(r"fwd16_kernelILb[01]ELi64ELb[01]ELi[12]ELb1E")
 
 
 def _function_asm(asm, name):

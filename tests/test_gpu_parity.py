@@ -273,8 +273,9 @@ def test_two_query_block_kernel(ea, oracle_lib, dtype):
 @pytest.mark.parametrize("dtype,d,n,causal", [
     (torch.bfloat16, 64, 131072, True),
     (torch.float16, 128, 65535, False),
+    (torch.float16, 64, 40000, True),    # past the fp16 first pass's 16384 keys
     (torch.float32, 64, 32768, True),
-], ids=["bf16-d64-128k-causal", "f16-d128-64k-ragged", "f32-d64-32k-causal"])
+], ids=["bf16-d64-128k-causal", "f16-d128-64k-ragged", "f16-d64-40k-causal", "f32-d64-32k-causal"])
 def test_long_sequence(ea, oracle_lib, dtype, d, n, causal):
     """Sequence lengths far past the workloads (one slice): positions and
     offsets stay exact; sampled rows across the whole range, the last rows
