@@ -26,10 +26,11 @@
 // gfx950 design (not the pages'):
 //   * 512 threads = 8 wave64s; each wave owns QB blocks of 32 query rows,
 //     QB = 1 or 2 (2 only at d = 64, where the registers hold two blocks).
-//     The launcher takes QB = 2 for long non-causal runs (twice the reuse of
-//     every K/V fragment) and QB = 1 under a causal mask (half as many
-//     diagonal tiles per work item) or when QB = 2 would leave compute units
-//     without a work item. K/V tiles hold 64 keys.
+//     The launcher takes QB = 2 for long runs (twice the reuse of every K/V
+//     fragment), under a causal mask only from 8192 keys on, and QB = 1 for
+//     shorter causal runs (half as many diagonal tiles per work item) or
+//     when QB = 2 would leave compute units without a work item. K/V tiles
+//     hold 64 keys.
 //   * Both products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32
 //     accumulation, in transposed form so that one lane owns one query:
 //        S^T[key][query] = K . Q^T     (A = K rows from LDS, B = Q in VGPRs)
@@ -828,21 +829,25 @@ hipError_t launch_qb(FwdParams p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Two query blocks per wave only without a causal mask, at d = 64, and when
-// their work items still cover every compute unit (measured: +2.5 to +6 %
-// on long non-causal runs; under a causal mask one block is 3 % faster at
-// the causal workloads, and on short sequences one block is up to 50 %
-// faster through the doubled item count).
+// Two query blocks per wave only at d = 64, when their work items still
+// cover every compute unit, and under a causal mask only from 8192 keys on
+// (measured: +2.5 to +6 % on long non-causal runs; causal, bf16, against
+// one block: N = 2048 -5.4 %, 4096 -0.7 %, 8192 +3.0 %, 16384 +4.5 %: the
+// 512-row items' diagonal tiles, whose dead waves no second workgroup on
+// the compute unit fills, weigh less in longer items; on short sequences
+// one block is up to 50 % faster through the doubled item count).
+constexpr int64_t kCausalTwoBlockMinN = 8192;
+
 template <bool IS_BF16, int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t s) {
-    if constexpr (D == 64 && !CAUSAL) {
+    if constexpr (D == 64) {
         const int64_t items2 = (p.N + block_m<2>() - 1) / block_m<2>() * p.BH;
-        const bool two = p.force_qb == 0 ? items2 >= kComputeUnits : p.force_qb == 2;
+        const bool automatic = items2 >= kComputeUnits && (!CAUSAL || p.N >= kCausalTwoBlockMinN);
+        const bool two = p.force_qb == 0 ? automatic : p.force_qb == 2;
         if (two) return launch_qb<IS_BF16, D, CAUSAL, 2>(p, s);
     }
     return launch_qb<IS_BF16, D, CAUSAL, 1>(p, s);
 }
-
 }  // namespace
 
 hipError_t launch_fwd16(const FwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s) {

@@ -101,7 +101,7 @@ def test_scratch_only_around_the_exact_pass_call(compiled):
     path, the tile loop included, spills nothing."""
     asm = compiled["fwd_mfma16.hip"][0]
     names = [k for k in compiled["fwd_mfma16.hip"][1] if CALLS_EXACT_PASS.search(k)]
-    assert len(names) == 6, names
+    assert len(names) == 8, names
     for name in names:
         blocks = _blocks(_function_asm(asm, name))
         calls = [b for b in blocks if "s_swappc_b64" in b]

@@ -313,6 +313,34 @@ def test_two_query_block_running_max(ea, oracle_lib, kind, dtype):
     assert err_l <= tol_l, err_l
 
 
+@pytest.mark.parametrize("kind", ["random", "spikes"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_causal_two_query_block_kernel(ea, oracle_lib, kind, dtype):
+    """Under a causal mask the launcher takes two query blocks per wave from
+    8192 keys on (B1 H32 N8192: 512 items of 512 rows): i.i.d. inputs, and
+    spike rows whose maximum jumps past fp32's exp2 range inside one tile
+    (their items take the exact pass); sampled rows of the first, middle
+    and last slice (item and diagonal boundaries included) and random ones
+    against the oracle."""
+    B, H, n, d = 1, 32, 8192, 64
+    if kind == "random":
+        q, k, v = make_qkv(B, H, n, d, dtype, seed=5400)
+    else:
+        q, k, v = make_structured_qkv("spikes", B, H, n, d, dtype, seed=5400)
+    scale = ea.default_scale(d)
+    o, lse = _run_gpu(ea, q, k, v, True, scale)
+    rows = _sample_rows(B, H, n, np.random.default_rng(5400), n_random=64)
+    rows = np.unique(np.concatenate([rows, (H // 2) * n + np.array([511, 512, 4095, 4096, 8190])]))
+    o_ref, lse_ref = oracle_lib.attn_fwd_ref_rows(q, k, v, True, scale, rows)
+    err_o = float(np.abs(o.reshape(-1, d)[rows] - o_ref).max())
+    err_l = float(np.abs(lse.reshape(-1)[rows] - lse_ref).max())
+    tol_l = lse_tol(dtype, n) + _score_term(q, k, scale)
+    print(f"causal two query blocks {kind} {dtype} ({len(rows)} sampled rows): O max-abs {err_o:.3e}, "
+          f"lse max-abs {err_l:.3e} (bound {tol_l:.3e})", flush=True)
+    assert np.all(np.isfinite(o)) and err_o <= O_TOL[dtype], err_o
+    assert err_l <= tol_l, err_l
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 def test_forced_variants_are_bit_identical(ea, dtype):
     """Every forward variant computes each row with the same arithmetic in

@@ -90,6 +90,16 @@ def test_forward_two_query_blocks_matches_probe_build(libs, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_forward_causal_two_query_blocks_matches_probe_build(libs, dtype):
+    """A causal grid long enough for the two-query-block kernel (from 8192
+    keys on; B1 H32 N8192: 512 items of 512 rows)."""
+    ea, lib, probe = libs
+    q, k, v = (t.cuda() for t in make_qkv(1, 32, 8192, 64, dtype, seed=7360))
+    _same(_fwd(ea, lib, q, k, v, True), _fwd(ea, probe, q, k, v, True),
+          f"forward causal two query blocks {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 @pytest.mark.parametrize("causal,H", [(False, 4), (True, 4), (False, 64)],
                          ids=["full", "causal", "full-two-query-blocks"])
 def test_forward_exact_pass_matches_probe_build(libs, causal, H, dtype):
