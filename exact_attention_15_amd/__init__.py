@@ -75,6 +75,8 @@ def _configure(lib):
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_debug_set_fwd_variant.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.attn_debug_set_fwd_variant.restype = ctypes.c_int
+    lib.attn_debug_set_fwd_first_pass.argtypes = [ctypes.c_int]
+    lib.attn_debug_set_fwd_first_pass.restype = ctypes.c_int
     return lib
 
 
@@ -91,6 +93,17 @@ def debug_set_fwd_variant(query_blocks: int = 0, order: int = 0) -> None:
     rc = load_library().attn_debug_set_fwd_variant(int(query_blocks), int(order))
     if rc != ATTN_OK:
         raise AttnError(rc, strerror(rc), "attn_debug_set_fwd_variant")
+
+
+def debug_set_fwd_first_pass(mode: int = 0) -> None:
+    """Debugging and testing only: at d = 64 force the 16-bit forward's
+    first pass without the per-tile overflow test (0 automatic, 1 the exact
+    pass only, 2 the first pass at any sequence length) for every later call
+    in the process; outputs are bit-identical across modes.
+    `debug_set_fwd_first_pass()` restores the automatic choice."""
+    rc = load_library().attn_debug_set_fwd_first_pass(int(mode))
+    if rc != ATTN_OK:
+        raise AttnError(rc, strerror(rc), "attn_debug_set_fwd_first_pass")
 
 
 def dtype_code(dtype) -> int:
@@ -281,5 +294,5 @@ def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, works
     return o, lse
 
 
-__all__ = ["fwd", "bwd", "debug_set_fwd_variant", "fwd_unfused", "attn_fwd_unfused", "unfused_workspace_bytes", "attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
+__all__ = ["fwd", "bwd", "debug_set_fwd_variant", "debug_set_fwd_first_pass", "fwd_unfused", "attn_fwd_unfused", "unfused_workspace_bytes", "attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_gqa", "load_library", "strerror", "AttnError", "default_scale",
            "dtype_code", "LIB_PATH", "ATTN_F32", "ATTN_F16", "ATTN_BF16"]

@@ -53,6 +53,8 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
 // Variant overrides of attn_debug_set_fwd_variant (0: automatic).
 std::atomic<int> g_force_qb{0};
 std::atomic<int> g_force_order{0};
+// Override of attn_debug_set_fwd_first_pass (0: automatic).
+std::atomic<int> g_force_first{0};
 
 }  // namespace
 
@@ -86,7 +88,8 @@ extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o
     if (dtype == ATTN_F32)
         e = attn::launch_fwd32(p, (int)d, causal != 0, s);
     else
-        e = attn::launch_fwd16(p, dtype == ATTN_BF16, (int)d, causal != 0, s);
+        e = attn::launch_fwd16(p, dtype == ATTN_BF16, (int)d, causal != 0,
+                              g_force_first.load(std::memory_order_relaxed), s);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
@@ -238,6 +241,12 @@ extern "C" int attn_debug_set_fwd_variant(int query_blocks, int order) {
     if (query_blocks < 0 || query_blocks > 2 || order < 0 || order > 2) return ATTN_EINVAL;
     g_force_qb.store(query_blocks, std::memory_order_relaxed);
     g_force_order.store(order, std::memory_order_relaxed);
+    return ATTN_OK;
+}
+
+extern "C" int attn_debug_set_fwd_first_pass(int mode) {
+    if (mode < 0 || mode > 2) return ATTN_EINVAL;
+    g_force_first.store(mode, std::memory_order_relaxed);
     return ATTN_OK;
 }
 

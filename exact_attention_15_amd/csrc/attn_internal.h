@@ -105,7 +105,14 @@ struct UnfusedParams {
 constexpr int kMinBlockM = 64;
 
 // Launchers return the hipError_t of the launch.
-hipError_t launch_fwd16(const FwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s);
+// force_first: 0 automatic, 1 exact pass only, 2 first pass at any N
+// (attn_debug_set_fwd_first_pass). It stays out of FwdParams: the d = 64
+// kernels hand FwdParams by value to their out-of-line exact pass, and one
+// more word there made that call take the work-item ids and the dispatch
+// pointer along: 6.7 % slower at B4 H16 N4096 d64 causal bf16 and 1.0 %
+// at B1 H8 N16384 d64 fp16 (same machine, both builds alternating).
+hipError_t launch_fwd16(const FwdParams& p, bool is_bf16, int d, bool causal, int force_first,
+                        hipStream_t s);
 hipError_t launch_fwd32(const FwdParams& p, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd16(const BwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s);
 hipError_t launch_bwd32(const BwdParams& p, int d, bool causal, hipStream_t s);

@@ -802,7 +802,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 4 : 1) void fwd16_
 constexpr int64_t kFp16FirstPassMaxN = 16384;
 
 template <bool IS_BF16, int D, bool CAUSAL, int QB>
-hipError_t launch_qb(FwdParams p, hipStream_t s) {
+hipError_t launch_qb(FwdParams p, int force_first, hipStream_t s) {
     p.n_qtiles = (int)((p.N + block_m<QB>() - 1) / block_m<QB>());
     // XCD-major order only without a causal mask, where every item is as
     // long as every other: measured at B1 H32 N8192 d128 it cuts the L2
@@ -819,13 +819,13 @@ hipError_t launch_qb(FwdParams p, hipStream_t s) {
     // alone, and the call into the exact pass costs more than that there)
     // the exact pass only.
     if constexpr (D == 64) {
-        if (IS_BF16 || p.N <= kFp16FirstPassMaxN) {
+        const bool first = force_first == 0 ? (IS_BF16 || p.N <= kFp16FirstPassMaxN) : force_first == 2;
+        if (first) {
             hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL, QB, true>), grid, dim3(kThreads), 0, s, p);
             return hipGetLastError();
         }
     }
-    if constexpr (!(D == 64 && IS_BF16))
-        hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL, QB, false>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd16_kernel<IS_BF16, D, CAUSAL, QB, false>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -839,24 +839,26 @@ hipError_t launch_qb(FwdParams p, hipStream_t s) {
 constexpr int64_t kCausalTwoBlockMinN = 8192;
 
 template <bool IS_BF16, int D, bool CAUSAL>
-hipError_t launch(const FwdParams& p, hipStream_t s) {
+hipError_t launch(const FwdParams& p, int force_first, hipStream_t s) {
     if constexpr (D == 64) {
         const int64_t items2 = (p.N + block_m<2>() - 1) / block_m<2>() * p.BH;
         const bool automatic = items2 >= kComputeUnits && (!CAUSAL || p.N >= kCausalTwoBlockMinN);
         const bool two = p.force_qb == 0 ? automatic : p.force_qb == 2;
-        if (two) return launch_qb<IS_BF16, D, CAUSAL, 2>(p, s);
+        if (two) return launch_qb<IS_BF16, D, CAUSAL, 2>(p, force_first, s);
     }
-    return launch_qb<IS_BF16, D, CAUSAL, 1>(p, s);
+    return launch_qb<IS_BF16, D, CAUSAL, 1>(p, force_first, s);
 }
 }  // namespace
 
-hipError_t launch_fwd16(const FwdParams& p, bool is_bf16, int d, bool causal, hipStream_t s) {
+hipError_t launch_fwd16(const FwdParams& p, bool is_bf16, int d, bool causal, int force_first,
+                        hipStream_t s) {
+    const int f = force_first;
     if (is_bf16) {
-        if (d == 64) return causal ? launch<true, 64, true>(p, s) : launch<true, 64, false>(p, s);
-        return causal ? launch<true, 128, true>(p, s) : launch<true, 128, false>(p, s);
+        if (d == 64) return causal ? launch<true, 64, true>(p, f, s) : launch<true, 64, false>(p, f, s);
+        return causal ? launch<true, 128, true>(p, f, s) : launch<true, 128, false>(p, f, s);
     }
-    if (d == 64) return causal ? launch<false, 64, true>(p, s) : launch<false, 64, false>(p, s);
-    return causal ? launch<false, 128, true>(p, s) : launch<false, 128, false>(p, s);
+    if (d == 64) return causal ? launch<false, 64, true>(p, f, s) : launch<false, 64, false>(p, f, s);
+    return causal ? launch<false, 128, true>(p, f, s) : launch<false, 128, false>(p, f, s);
 }
 
 }  // namespace attn

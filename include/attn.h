@@ -213,8 +213,7 @@ const char* attn_strerror(int code);
  *
  *   query_blocks  0: automatic; 1: one 32-row query block per wave (256-row
  *                 work items); 2: two blocks per wave (512-row items), which
- *                 only the d = 64 non-causal kernel has: elsewhere 2 acts as
- *                 0.
+ *                 only the d = 64 kernels have: at d = 128 2 acts as 0.
  *   order         0: automatic; 1: tile-major work order (longest query
  *                 tiles first, consecutive items on different slices);
  *                 2: XCD-major (each of the 8 XCDs takes its K/V slices one
@@ -227,6 +226,24 @@ const char* attn_strerror(int code);
  * changes nothing) for a value outside the ranges above. Makes no HIP call.
  */
 int attn_debug_set_fwd_variant(int query_blocks, int order);
+
+/*
+ * attn_debug_set_fwd_first_pass — debugging and testing only: at d = 64,
+ * fp16 and bf16, force whether attn_fwd / attn_fwd_gqa run the first pass
+ * without the per-tile overflow test (handing a work item to the exact pass
+ * when some row's l exceeds the rescale threshold), for every later call
+ * from any thread of the process, like attn_debug_set_fwd_variant.
+ *
+ *   mode  0: automatic (bf16 always; fp16 up to N = 16384 keys);
+ *         1: the exact pass only; 2: the first pass at any N.
+ *
+ * A row's first-pass result is kept only when its l shows that no
+ * probability exceeded the threshold, in which case the exact pass, which
+ * moves a row's exponent base only past that threshold, gives the same
+ * bits: outputs are bit-identical across modes. Returns ATTN_OK, or ATTN_EINVAL (and changes
+ * nothing) for a mode outside 0..2. Makes no HIP call.
+ */
+int attn_debug_set_fwd_first_pass(int mode);
 
 #ifdef __cplusplus
 }

@@ -45,9 +45,9 @@ def test_every_header_is_covered():
 
 def test_attn_library_exports_header(attn_lib_path):
     decl = _declared_functions("attn.h")
-    assert decl == ["attn_bwd", "attn_bwd_noalloc", "attn_debug_set_fwd_variant", "attn_fwd",
-                    "attn_fwd_gqa", "attn_fwd_unfused", "attn_strerror",
-                    "attn_unfused_workspace_bytes"]
+    assert decl == ["attn_bwd", "attn_bwd_noalloc", "attn_debug_set_fwd_first_pass",
+                    "attn_debug_set_fwd_variant", "attn_fwd", "attn_fwd_gqa", "attn_fwd_unfused",
+                    "attn_strerror", "attn_unfused_workspace_bytes"]
     missing = set(decl) - _exported(attn_lib_path)
     assert not missing, missing
     ctypes.CDLL(attn_lib_path)   # loads without a GPU
@@ -96,6 +96,20 @@ def test_debug_variant_switch(attn_lib_path):
     with pytest.raises(ea.AttnError):
         ea.debug_set_fwd_variant(5, 0)
     ea.debug_set_fwd_variant()
+
+
+def test_debug_first_pass_switch(attn_lib_path):
+    """attn_debug_set_fwd_first_pass takes 0..2 (no HIP call) and rejects
+    anything else without changing the setting."""
+    import exact_attention_15_amd as ea
+    lib = ea.load_library()
+    for mode in (0, 1, 2, 0):
+        assert lib.attn_debug_set_fwd_first_pass(mode) == ea.ATTN_OK
+    for mode in (3, -1):
+        assert lib.attn_debug_set_fwd_first_pass(mode) == ea.ATTN_EINVAL
+    with pytest.raises(ea.AttnError):
+        ea.debug_set_fwd_first_pass(7)
+    ea.debug_set_fwd_first_pass()
 
 
 def test_strerror(attn_lib_path):

@@ -313,6 +313,42 @@ def test_two_query_block_running_max(ea, oracle_lib, kind, dtype):
     assert err_l <= tol_l, err_l
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_first_pass_modes_are_bit_identical(ea, dtype):
+    """At d = 64 the automatic choice (first pass without the per-tile
+    overflow test), the exact pass alone and the first pass at any length
+    (attn_debug_set_fwd_first_pass 0, 1, 2) give the same bits: on each
+    d = 64 kernel (one and two query blocks, causal and not, ragged N, a
+    grouped-query shape), at an fp16 length past the automatic first pass's
+    16384 keys, and on the full-size headline workload."""
+    cases = [(1, 8, 8, 1000, True), (1, 128, 128, 1000, False), (2, 4, 4, 777, False),
+             (1, 32, 32, 8192, True), (2, 16, 4, 640, True), (1, 2, 2, 17000, False)]
+    try:
+        for B, H, H_kv, n, causal in cases:
+            q, k, v = (t.cuda() for t in make_qkv(B, H, n, 64, dtype, seed=8900 + n, H_kv=H_kv))
+            outs = []
+            for mode in (0, 1, 2):
+                ea.debug_set_fwd_first_pass(mode)
+                outs.append(ea.fwd(q, k, v, causal=causal))
+            torch.cuda.synchronize()
+            same = all(torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1]) for o, l in outs[1:])
+            print(f"{dtype} B{B} H{H}/{H_kv} N{n} causal={causal}: modes 0/1/2 identical={same}", flush=True)
+            assert same, (B, H, H_kv, n, causal)
+        if dtype == torch.bfloat16:
+            w = WORKLOADS["c3_bf16_causal"]
+            q, k, v = (t.cuda() for t in workload_inputs(w))
+            outs = []
+            for mode in (0, 1):
+                ea.debug_set_fwd_first_pass(mode)
+                outs.append(ea.fwd(q, k, v, causal=w.causal, scale=w.scale))
+            torch.cuda.synchronize()
+            same = torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+            print(f"c3_bf16_causal: first pass and exact pass identical={same}", flush=True)
+            assert same
+    finally:
+        ea.debug_set_fwd_first_pass()
+
+
 @pytest.mark.parametrize("kind", ["random", "spikes"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 def test_causal_two_query_block_kernel(ea, oracle_lib, kind, dtype):
