@@ -237,11 +237,12 @@ int attn_debug_set_fwd_variant(int query_blocks, int order);
  *   mode  0: automatic (bf16 always; fp16 up to N = 16384 keys);
  *         1: the exact pass only; 2: the first pass at any N.
  *
- * A row's first-pass result is kept only when its l shows that no
- * probability exceeded the threshold, in which case the exact pass, which
- * moves a row's exponent base only past that threshold, gives the same
- * bits: outputs are bit-identical across modes. Returns ATTN_OK, or ATTN_EINVAL (and changes
- * nothing) for a mode outside 0..2. Makes no HIP call.
+ * A work item's first-pass result is kept only when every row's l shows
+ * that no probability exceeded the threshold, in which case the exact pass,
+ * which moves a row's exponent base only past that threshold, gives the
+ * same bits: outputs are bit-identical across modes. Returns ATTN_OK, or
+ * ATTN_EINVAL (and changes nothing) for a mode outside 0..2. Makes no HIP
+ * call.
  */
 int attn_debug_set_fwd_first_pass(int mode);
 
