@@ -99,8 +99,8 @@ def test_debug_variant_switch(attn_lib_path):
 
 
 def test_debug_first_pass_switch(attn_lib_path):
-    """attn_debug_set_fwd_first_pass takes 0..2 (no HIP call) and rejects
-    anything else without changing the setting."""
+    """attn_debug_set_fwd_first_pass takes 0..2 (no HIP call) and returns
+    ATTN_EINVAL for anything else; the wrapper raises on it."""
     import exact_attention_15_amd as ea
     lib = ea.load_library()
     for mode in (0, 1, 2, 0):
