@@ -234,7 +234,7 @@ int attn_debug_set_fwd_variant(int query_blocks, int order);
  * when some row's l exceeds the rescale threshold), for every later call
  * from any thread of the process, like attn_debug_set_fwd_variant.
  *
- *   mode  0: automatic (bf16 always; fp16 up to N = 16384 keys);
+ *   mode  0: automatic (bf16 always; fp16 up to N = 32768 keys);
  *         1: the exact pass only; 2: the first pass at any N.
  *
  * A work item's first-pass result is kept only when every row's l shows

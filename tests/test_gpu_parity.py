@@ -17,6 +17,8 @@ Small shapes are checked element by element on every output; the full-size
 workloads (in the launch configuration the bench times) on every row, or on
 every row of eight whole slices for the three d = 128, N = 8192 workloads.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -273,9 +275,11 @@ def test_two_query_block_kernel(ea, oracle_lib, dtype):
 @pytest.mark.parametrize("dtype,d,n,causal", [
     (torch.bfloat16, 64, 131072, True),
     (torch.float16, 128, 65535, False),
-    (torch.float16, 64, 40000, True),    # past the fp16 first pass's 16384 keys
+    (torch.float16, 64, 40000, True),    # past the fp16 first pass's 32768 keys
+    (torch.float16, 64, 32768, False),   # the fp16 first pass's longest rows
     (torch.float32, 64, 32768, True),
-], ids=["bf16-d64-128k-causal", "f16-d128-64k-ragged", "f16-d64-40k-causal", "f32-d64-32k-causal"])
+], ids=["bf16-d64-128k-causal", "f16-d128-64k-ragged", "f16-d64-40k-causal", "f16-d64-32k",
+        "f32-d64-32k-causal"])
 def test_long_sequence(ea, oracle_lib, dtype, d, n, causal):
     """Sequence lengths far past the workloads (one slice): positions and
     offsets stay exact; sampled rows across the whole range, the last rows
@@ -320,9 +324,11 @@ def test_first_pass_modes_are_bit_identical(ea, dtype):
     (attn_debug_set_fwd_first_pass 0, 1, 2) give the same bits: on each
     d = 64 kernel (one and two query blocks, causal and not, ragged N, a
     grouped-query shape), at an fp16 length past the automatic first pass's
-    16384 keys, and on the full-size headline workload."""
+    32768 keys, on flat fp16 rows of exactly 32768 keys (every P = 1, so
+    l = 2^15 sits on the first pass's l <= 2^15 check; O must be the mean
+    of V and lse ln N), and on the full-size headline workload."""
     cases = [(1, 8, 8, 1000, True), (1, 128, 128, 1000, False), (2, 4, 4, 777, False),
-             (1, 32, 32, 8192, True), (2, 16, 4, 640, True), (1, 2, 2, 17000, False)]
+             (1, 32, 32, 8192, True), (2, 16, 4, 640, True), (1, 2, 2, 33000, False)]
     try:
         for B, H, H_kv, n, causal in cases:
             q, k, v = (t.cuda() for t in make_qkv(B, H, n, 64, dtype, seed=8900 + n, H_kv=H_kv))
@@ -334,6 +340,22 @@ def test_first_pass_modes_are_bit_identical(ea, dtype):
             same = all(torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1]) for o, l in outs[1:])
             print(f"{dtype} B{B} H{H}/{H_kv} N{n} causal={causal}: modes 0/1/2 identical={same}", flush=True)
             assert same, (B, H, H_kv, n, causal)
+        if dtype == torch.float16:
+            n = 32768
+            q, k, v = (t.cuda() for t in make_qkv(1, 2, n, 64, dtype, seed=8950))
+            q.zero_()
+            outs = []
+            for mode in (0, 1, 2):
+                ea.debug_set_fwd_first_pass(mode)
+                outs.append(ea.fwd(q, k, v))
+            torch.cuda.synchronize()
+            same = all(torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1]) for o, l in outs[1:])
+            mean_v = v.double().mean(dim=2, keepdim=True).expand(-1, -1, n, -1)
+            o_err = float((outs[0][0].double() - mean_v).abs().max())
+            lse_err = float((outs[0][1].double() - math.log(n)).abs().max())
+            print(f"flat f16 N{n}: modes identical={same}, O vs mean of V {o_err:.2e}, "
+                  f"lse vs ln N {lse_err:.2e}", flush=True)
+            assert same and o_err <= O_TOL[dtype] and lse_err <= 1e-5
         if dtype == torch.bfloat16:
             w = WORKLOADS["c3_bf16_causal"]
             q, k, v = (t.cuda() for t in workload_inputs(w))
